@@ -1,0 +1,60 @@
+"""Algorithmic work of each call: the bytes or flop the method must move or compute.
+
+These are the roofline numerators.  They count what the operation itself needs:
+no split-K workspace traffic, no masked or padded work, no re-reads.
+
+Sizing on the pages that pins the byte unit (「同一个 Qwen3，两种写法」 §2.2): K and V
+of one token over all 36 layers of Qwen3-8B (8 KV heads, head_dim 128, bf16) take
+2 * 36 * 8 * 128 * 2 = 147,456 bytes; a 256-token block is 36 MiB; a 40960-token
+context is about 6.0 GB.  Per layer that is 4096 B per token and 1 MiB per block.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """K plus V of one token across ``num_layers`` layers."""
+    return 2 * num_layers * num_kv_heads * head_dim * elem_bytes
+
+
+def store_bytes(slot_mapping, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """Read K and V rows of stored tokens, write them to the pool, read every slot."""
+    slots = np.asarray(slot_mapping)
+    written = int((slots != -1).sum())
+    return 4 * written * num_kv_heads * head_dim * elem_bytes + 4 * len(slots)
+
+
+def decode_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 block_size: int, elem_bytes: int) -> int:
+    """K/V of every cached position, q in, out back, context_lens and block ids."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    nblk = int(((lens + block_size - 1) // block_size).sum())
+    b = len(lens)
+    return (2 * elem_bytes * num_kv_heads * head_dim * int(lens.sum())
+            + 2 * b * num_q_heads * head_dim * elem_bytes
+            + 4 * (b + nblk))
+
+
+def prefill_pairs(cu_seqlens_q, cu_seqlens_k) -> int:
+    """Unmasked (query, key) pairs per Q head, bottom-right causal in each segment."""
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    lq = np.diff(cq)
+    lk = np.diff(ck)
+    return int((lq * (lk - lq) + lq * (lq + 1) // 2).sum())
+
+
+def prefill_flops(cu_seqlens_q, cu_seqlens_k, num_q_heads: int, head_dim: int) -> int:
+    """2*D flop for q.k and 2*D for p*v, per unmasked pair and Q head."""
+    return 4 * head_dim * num_q_heads * prefill_pairs(cu_seqlens_q, cu_seqlens_k)
+
+
+def prefill_min_bytes(cu_seqlens_q, cu_seqlens_k, num_q_heads: int, num_kv_heads: int,
+                      head_dim: int, elem_bytes: int) -> int:
+    """q read once, out written once, each sequence's K/V read once."""
+    tq = int(np.asarray(cu_seqlens_q)[-1])
+    tk = int(np.asarray(cu_seqlens_k)[-1])
+    return (2 * tq * num_q_heads * head_dim * elem_bytes
+            + 2 * tk * num_kv_heads * head_dim * elem_bytes)
