@@ -1,0 +1,179 @@
+/*
+ * nkv.h -- C ABI of libnkv.so: the paged KV-cache data plane on AMD MI355X (gfx950).
+ *
+ * Three operations, named after the calls they replace in nano-vLLM's
+ * Attention.forward (「Nano-vLLM深度解读（下）」 §4, attention.py listing):
+ *
+ *   nkv_store_kvcache       store_kvcache(k, v, k_cache, v_cache, slot_mapping)
+ *   nkv_paged_attn_prefill  flash_attn_varlen_func(q, k_cache, v_cache, cu_seqlens_q/k,
+ *                           max_seqlen_q/k, softmax_scale, causal=True, block_table)
+ *   nkv_paged_attn_decode   flash_attn_with_kvcache(q.unsqueeze(1), k_cache, v_cache,
+ *                           cache_seqlens=context_lens, block_table, softmax_scale,
+ *                           causal=True)
+ *
+ * Data layout (「同一个 Qwen3，两种写法」 §3.3, the pool allocated once at start-up):
+ *   one layer's K pool and V pool are each a contiguous
+ *   [num_blocks, block_size, num_kv_heads, head_dim] array, so a cache row ("slot")
+ *   is num_kv_heads*head_dim contiguous elements and slot = physical_block *
+ *   block_size + offset_in_block.  Every pointer argument is a DEVICE pointer except
+ *   where stated; sizes are element counts unless stated.
+ *
+ * Ownership and ordering:
+ *   - the caller owns every buffer; the library allocates nothing and keeps no state
+ *     between calls (it caches the device's compute-unit count per device);
+ *   - every call is asynchronous and ordered on `stream` (a hipStream_t passed as
+ *     void*, NULL = the legacy default stream); nothing is read back to the host;
+ *   - attention never writes the pools; the store writes only the rows that
+ *     slot_mapping names; `out` is fully overwritten and must not alias any input;
+ *   - store before attention is the caller's job (the new token's K/V must be in the
+ *     pool before the decode or prefix-cached prefill that reads it).
+ *
+ * Errors: every function returns a status and never aborts.  Arguments the host can
+ * check (null pointers with non-zero sizes, dtype, head counts, head_dim, block_size,
+ * strides, alignment, workspace size) are always checked and rejected with
+ * NKV_ERR_INVALID_ARG or NKV_ERR_UNSUPPORTED before anything is launched.  The
+ * contents of device-resident index arrays are preconditions, as in the reference
+ * store kernel: slots in [0, num_blocks*block_size) or -1 and unique within a call;
+ * block ids in [0, num_blocks) for every logical block a sequence uses;
+ * 1 <= context_lens[b] <= max_blocks_per_seq*block_size; cu_seqlens non-decreasing
+ * with 0 <= Lq <= Lk per sequence.  A launch failure returns NKV_ERR_HIP.
+ * nkv_last_error() gives a human-readable reason for the last failure on the
+ * calling thread.
+ */
+#ifndef NKV_H
+#define NKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NKV_ABI_VERSION 1
+
+typedef enum {
+  NKV_OK = 0,
+  NKV_ERR_INVALID_ARG = 1, /* a host-checkable argument is wrong                  */
+  NKV_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels are built for    */
+  NKV_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required    */
+  NKV_ERR_HIP = 4          /* the HIP runtime reported an error                     */
+} nkv_status_t;
+
+typedef enum {
+  NKV_F32 = 0,  /* IEEE binary32                                 */
+  NKV_BF16 = 1  /* bfloat16 (upper 16 bits of a binary32)        */
+} nkv_dtype_t;
+
+/* Version of this header's ABI (NKV_ABI_VERSION the library was built with). */
+int nkv_abi_version(void);
+
+/* Static string naming a status code. */
+const char* nkv_status_string(nkv_status_t status);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char* nkv_last_error(void);
+
+/*
+ * Scatter new K/V rows into one layer's paged pools through slot_mapping.
+ * 「Nano-vLLM深度解读（下）」 §4 (store_kvcache_kernel / store_kvcache): token t with
+ * slot s = slot_mapping[t] copies key[t] (num_kv_heads*head_dim elements) to row s of
+ * k_cache and value[t] to row s of v_cache; s == -1 skips the token.  The copy is bit
+ * exact (no conversion).
+ *
+ *   key, value        [num_tokens, num_kv_heads, head_dim]; the last two dims are
+ *                     contiguous; rows are key_row_stride / value_row_stride ELEMENTS
+ *                     apart (>= num_kv_heads*head_dim, e.g. a k/v view cut from a packed
+ *                     qkv projection output).  Base pointers and row strides must be
+ *                     16-byte aligned.
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim], contiguous,
+ *                     16-byte aligned.
+ *   slot_mapping      [num_tokens] int32.
+ *   num_tokens == 0 is a no-op.
+ */
+nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_stride,
+                               const void* value, int64_t value_row_stride,
+                               void* k_cache, void* v_cache,
+                               const int32_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t num_blocks, int32_t block_size,
+                               nkv_dtype_t dtype, void* stream);
+
+/*
+ * Causal varlen prefill attention over the paged pools.
+ * 「同一个 Qwen3，两种写法」 §3.2 (flat [T, H, D] batch split by cu_seqlens, causal inside
+ * each segment, nothing computed across segments) and §3.4 (GQA inside the kernel; K/V
+ * read from the paged cache through the block table).  For sequence b:
+ *   queries  q[cu_seqlens_q[b] .. cu_seqlens_q[b+1])            (Lq of them)
+ *   keys     its first Lk = cu_seqlens_k[b+1]-cu_seqlens_k[b] positions in the pool,
+ *            position p in block block_table[b*max_blocks_per_seq + p/block_size]
+ *   query i (0-based) attends to keys j <= Lk - Lq + i (bottom-right alignment: a
+ *   chunk of new tokens follows the cached prefix); Q head h uses KV head
+ *   h / (num_q_heads/num_kv_heads).
+ *   out[i, h, :] = sum_j softmax_j(softmax_scale * q_i.k_j) v_j, fp32 accumulation.
+ *
+ *   q           [total_q, num_q_heads, head_dim], rows q_row_stride elements apart
+ *               (>= num_q_heads*head_dim, 16-byte aligned), same dtype as the pools.
+ *   out         [total_q, num_q_heads, head_dim] contiguous, dtype of q.
+ *   cu_seqlens_q, cu_seqlens_k  [num_seqs+1] int32;  block_table
+ *               [num_seqs, max_blocks_per_seq] int32 (entries past a sequence's last
+ *               block are never read).
+ *   max_seqlen_q / max_seqlen_k: host upper bounds of Lq / Lk (size the grid).
+ *   Supported: head_dim 64 or 128; num_q_heads/num_kv_heads in {1,2,4,8};
+ *   block_size a power of two in [16, 1024]; bf16 (MFMA path) or fp32 (VALU path).
+ */
+nkv_status_t nkv_paged_attn_prefill(const void* q, int64_t q_row_stride,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    int32_t num_seqs, int32_t total_q,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t num_blocks, int32_t block_size,
+                                    float softmax_scale, nkv_dtype_t dtype,
+                                    void* out, void* stream);
+
+/*
+ * Bytes of device workspace nkv_paged_attn_decode needs for these sizes (split-K
+ * partial results).  Depends on the current device's compute-unit count.
+ */
+size_t nkv_paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t max_blocks_per_seq, int32_t block_size);
+
+/*
+ * Single-token decode attention over the paged pools.
+ * 「Nano-vLLM深度解读（下）」 §4 and 「同一个 Qwen3，两种写法」 §3.4 (flash_attn_with_kvcache
+ * with cache_seqlens and block_table): the one query of sequence b attends to all of
+ * its context_lens[b] cached positions (which include the token stored just before
+ * this call); Q head h uses KV head h / (num_q_heads/num_kv_heads).
+ *
+ *   q             [num_seqs, num_q_heads, head_dim] contiguous, pool dtype.
+ *   context_lens  [num_seqs] int32, each in [1, max_blocks_per_seq*block_size].
+ *   block_table   [num_seqs, max_blocks_per_seq] int32.
+ *   out           [num_seqs, num_q_heads, head_dim] contiguous, dtype of q.
+ *   workspace     device buffer of at least nkv_paged_attn_decode_workspace_size(...)
+ *                 bytes, 16-byte aligned (may be NULL when that size is 0); its
+ *                 contents on entry do not matter.  Calls that share a workspace must
+ *                 be ordered on one stream.
+ *   Long contexts are split over several workgroups ("split-K"), each producing a
+ *   partial (max, sum, weighted values) that a second kernel merges; splits depend
+ *   only on logical positions, so results are bitwise reproducible and do not depend
+ *   on which physical blocks hold the data.
+ *   Supported: as for prefill (bf16 and fp32 both on the VALU path).
+ */
+nkv_status_t nkv_paged_attn_decode(const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* context_lens,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                                   float softmax_scale, nkv_dtype_t dtype,
+                                   void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* NKV_H */

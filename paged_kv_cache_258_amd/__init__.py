@@ -1,0 +1,25 @@
+"""nkv: the paged KV-cache data plane (store, paged prefill, paged decode) for MI355X.
+
+The compute lives in ``libnkv.so`` (HIP kernels for gfx950 behind the C ABI of
+``include/nkv.h``); this package is its thin Python binding plus the seeded input
+generators (``workloads``) and the algorithmic byte/flop accounting (``accounting``).
+The library is loaded on first use and the calls raise if it is not built.
+"""
+
+from ._lib import (  # noqa: F401
+    NkvError,
+    load,
+    nkv_paged_attn_decode,
+    nkv_paged_attn_decode_workspace_size,
+    nkv_paged_attn_prefill,
+    nkv_store_kvcache,
+)
+
+__all__ = [
+    "NkvError",
+    "load",
+    "nkv_store_kvcache",
+    "nkv_paged_attn_prefill",
+    "nkv_paged_attn_decode",
+    "nkv_paged_attn_decode_workspace_size",
+]

@@ -1,0 +1,207 @@
+"""ctypes binding of libnkv.so (include/nkv.h).
+
+Argument marshalling only: every step of the data plane runs in the HIP kernels of
+the library.  Torch tensors supply device memory (``data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``).  The functions carry the C names.
+If the library is missing the first call raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnkv.so")
+
+NKV_OK, NKV_ERR_INVALID_ARG, NKV_ERR_UNSUPPORTED, NKV_ERR_WORKSPACE, NKV_ERR_HIP = range(5)
+NKV_F32, NKV_BF16 = 0, 1
+ABI_VERSION = 1
+
+EXPORTS = (
+    "nkv_abi_version",
+    "nkv_status_string",
+    "nkv_last_error",
+    "nkv_store_kvcache",
+    "nkv_paged_attn_prefill",
+    "nkv_paged_attn_decode_workspace_size",
+    "nkv_paged_attn_decode",
+)
+
+_lib = None
+
+
+class NkvError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS_NAMES.get(status, status)}: {detail}")
+
+
+_STATUS_NAMES = {0: "NKV_OK", 1: "NKV_ERR_INVALID_ARG", 2: "NKV_ERR_UNSUPPORTED",
+                 3: "NKV_ERR_WORKSPACE", 4: "NKV_ERR_HIP"}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libnkv.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m paged_kv_cache_258_amd.build`")
+    lib = ctypes.CDLL(path)
+    c_i32, c_i64, c_p, c_f = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    lib.nkv_abi_version.restype = ctypes.c_int
+    lib.nkv_abi_version.argtypes = []
+    lib.nkv_status_string.restype = ctypes.c_char_p
+    lib.nkv_status_string.argtypes = [ctypes.c_int]
+    lib.nkv_last_error.restype = ctypes.c_char_p
+    lib.nkv_last_error.argtypes = []
+    lib.nkv_store_kvcache.restype = ctypes.c_int
+    lib.nkv_store_kvcache.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_p, c_p, c_i32,
+                                      c_i32, c_i32, c_i32, c_i32, ctypes.c_int, c_p]
+    lib.nkv_paged_attn_prefill.restype = ctypes.c_int
+    lib.nkv_paged_attn_prefill.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i32,
+                                           c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                           c_i32, c_i32, c_f, ctypes.c_int, c_p, c_p]
+    lib.nkv_paged_attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.nkv_paged_attn_decode_workspace_size.argtypes = [c_i32] * 6
+    lib.nkv_paged_attn_decode.restype = ctypes.c_int
+    lib.nkv_paged_attn_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32,
+                                          c_i32, c_i32, c_i32, c_f, ctypes.c_int, c_p, c_p,
+                                          ctypes.c_size_t, c_p]
+    if lib.nkv_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libnkv.so ABI {lib.nkv_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != NKV_OK:
+        raise NkvError(status, where, load().nkv_last_error().decode())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return NKV_BF16
+    if t.dtype == torch.float32:
+        return NKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _int32_dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def _pool_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache/v_cache must both be [num_blocks, block_size, num_kv_heads, head_dim]")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("pools must be contiguous")
+    return tuple(int(x) for x in k_cache.shape)
+
+
+# ---------------------------------------------------------------------------------------
+# the three operations (same names as the C ABI)
+# ---------------------------------------------------------------------------------------
+
+def nkv_store_kvcache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Scatter key/value rows [N, Hkv, D] into the pools at slot_mapping (-1 = skip)."""
+    lib = load()
+    n, hkv, d = key.shape
+    if value.shape != key.shape:
+        raise ValueError("key and value shapes differ")
+    if key.stride(2) != 1 or key.stride(1) != d or value.stride(2) != 1 or value.stride(1) != d:
+        raise ValueError("key/value need contiguous [Hkv, D] rows")
+    nb, bs, phkv, pd = _pool_dims(k_cache, v_cache)
+    if (phkv, pd) != (hkv, d):
+        raise ValueError("pool head shape differs from key/value")
+    _int32_dev(slot_mapping, "slot_mapping")
+    if slot_mapping.numel() != n:
+        raise ValueError("slot_mapping must have one entry per token")
+    _check(lib.nkv_store_kvcache(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
+                                 _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), n, hkv, d,
+                                 nb, bs, _dtype(key), _stream(key)), "nkv_store_kvcache")
+
+
+def nkv_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                           block_table: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                           softmax_scale: float, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal varlen prefill over the paged pools; returns out [Tq, Hq, D]."""
+    lib = load()
+    tq, hq, d = q.shape
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q needs contiguous [Hq, D] rows")
+    nb, bs, hkv, pd = _pool_dims(k_cache, v_cache)
+    if pd != d:
+        raise ValueError("head_dim of q and pools differ")
+    _int32_dev(cu_seqlens_q, "cu_seqlens_q")
+    _int32_dev(cu_seqlens_k, "cu_seqlens_k")
+    _int32_dev(block_table, "block_table")
+    nseq = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != nseq + 1 or block_table.dim() != 2 or block_table.shape[0] != nseq:
+        raise ValueError("cu_seqlens_q/k must be [B+1] and block_table [B, max_blocks]")
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=q.dtype, device=q.device)
+    elif out.shape != (tq, hq, d) or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous [Tq, Hq, D] tensor of q's dtype")
+    _check(lib.nkv_paged_attn_prefill(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(block_table),
+                                      block_table.shape[1], nseq, tq, int(max_seqlen_q),
+                                      int(max_seqlen_k), hq, hkv, d, nb, bs, float(softmax_scale),
+                                      _dtype(q), _ptr(out), _stream(q)),
+           "nkv_paged_attn_prefill")
+    return out
+
+
+def nkv_paged_attn_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                         head_dim: int, max_blocks_per_seq: int,
+                                         block_size: int) -> int:
+    return int(load().nkv_paged_attn_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                           head_dim, max_blocks_per_seq,
+                                                           block_size))
+
+
+def nkv_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          context_lens: torch.Tensor, block_table: torch.Tensor,
+                          softmax_scale: float, out: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Single-token decode over the paged pools; q [B, Hq, D] -> out [B, Hq, D]."""
+    lib = load()
+    nseq, hq, d = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    nb, bs, hkv, pd = _pool_dims(k_cache, v_cache)
+    if pd != d:
+        raise ValueError("head_dim of q and pools differ")
+    _int32_dev(context_lens, "context_lens")
+    _int32_dev(block_table, "block_table")
+    if context_lens.numel() != nseq or block_table.dim() != 2 or block_table.shape[0] != nseq:
+        raise ValueError("context_lens must be [B] and block_table [B, max_blocks]")
+    maxb = block_table.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    need = nkv_paged_attn_decode_workspace_size(nseq, hq, hkv, d, maxb, bs)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.nkv_paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(context_lens),
+                                     _ptr(block_table), maxb, nseq, hq, hkv, d, nb, bs,
+                                     float(softmax_scale), _dtype(q), _ptr(out), _ptr(workspace),
+                                     ws_bytes, _stream(q)),
+           "nkv_paged_attn_decode")
+    return out

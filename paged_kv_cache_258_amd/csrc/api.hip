@@ -1,0 +1,238 @@
+// C ABI of libnkv.so (declared in include/nkv.h): argument checks, then launches.
+//
+// Only host-checkable arguments are validated here; the contents of device-resident
+// index arrays are preconditions of the kernels (as in the reference store kernel,
+// 「Nano-vLLM深度解读（下）」 §4, which only tests for slot == -1).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/nkv.h"
+#include "launch.hpp"
+
+#define NKV_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+nkv_status_t fail(nkv_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+nkv_status_t ok() {
+  g_last_error[0] = '\0';
+  return NKV_OK;
+}
+
+nkv_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(NKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Compute-unit count of the current device, cached per device.
+int num_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ilog2_exact(int x) {
+  if (x <= 0 || (x & (x - 1)) != 0) return -1;
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+int elem_bytes(nkv_dtype_t dt) { return dt == NKV_BF16 ? 2 : 4; }
+
+// Checks shared by prefill and decode; fills the common launch descriptor.
+nkv_status_t check_paged(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                         int32_t block_size, float softmax_scale, nkv_dtype_t dtype,
+                         nkv::PagedArgs* pa) {
+  if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  if (num_seqs < 0) return fail(NKV_ERR_INVALID_ARG, "num_seqs < 0");
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(NKV_ERR_INVALID_ARG, "head counts must be positive");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(NKV_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  const int grp = num_q_heads / num_kv_heads;
+  if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
+    return fail(NKV_ERR_UNSUPPORTED, "GQA group size %d not in {1,2,4,8}", grp);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(NKV_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  const int lb = ilog2_exact(block_size);
+  if (lb < 4 || lb > 10)
+    return fail(NKV_ERR_UNSUPPORTED, "block_size %d is not a power of two in [16,1024]", block_size);
+  if (num_blocks <= 0) return fail(NKV_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (int64_t(num_blocks) * block_size > int64_t(INT32_MAX))
+    return fail(NKV_ERR_UNSUPPORTED, "pool has more than 2^31-1 rows");
+  if (max_blocks_per_seq <= 0) return fail(NKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (int64_t(max_blocks_per_seq) * block_size > int64_t(INT32_MAX))
+    return fail(NKV_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size exceeds 2^31-1");
+  if (!(softmax_scale == softmax_scale) || softmax_scale < 0.f)
+    return fail(NKV_ERR_INVALID_ARG, "softmax_scale must be a non-negative number");
+  if (num_seqs > 0 && (!k_cache || !v_cache || !block_table))
+    return fail(NKV_ERR_INVALID_ARG, "null pool or block_table pointer");
+  if (num_seqs > 0 && (!aligned16(k_cache) || !aligned16(v_cache)))
+    return fail(NKV_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  pa->k_cache = k_cache;
+  pa->v_cache = v_cache;
+  pa->block_table = block_table;
+  pa->max_blocks_per_seq = max_blocks_per_seq;
+  pa->num_seqs = num_seqs;
+  pa->num_q_heads = num_q_heads;
+  pa->num_kv_heads = num_kv_heads;
+  pa->head_dim = head_dim;
+  pa->block_size = block_size;
+  pa->log2_block_size = lb;
+  pa->scale_log2e = softmax_scale * 1.4426950408889634f;
+  pa->dtype = dtype == NKV_BF16 ? nkv::Dtype::BF16 : nkv::Dtype::F32;
+  pa->num_cus = num_cus();
+  return NKV_OK;
+}
+
+}  // namespace
+
+NKV_EXPORT int nkv_abi_version(void) { return NKV_ABI_VERSION; }
+
+NKV_EXPORT const char* nkv_status_string(nkv_status_t s) {
+  switch (s) {
+    case NKV_OK: return "NKV_OK";
+    case NKV_ERR_INVALID_ARG: return "NKV_ERR_INVALID_ARG";
+    case NKV_ERR_UNSUPPORTED: return "NKV_ERR_UNSUPPORTED";
+    case NKV_ERR_WORKSPACE: return "NKV_ERR_WORKSPACE";
+    case NKV_ERR_HIP: return "NKV_ERR_HIP";
+  }
+  return "NKV_UNKNOWN_STATUS";
+}
+
+NKV_EXPORT const char* nkv_last_error(void) { return g_last_error; }
+
+NKV_EXPORT nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_stride,
+                                          const void* value, int64_t value_row_stride,
+                                          void* k_cache, void* v_cache,
+                                          const int32_t* slot_mapping, int32_t num_tokens,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t num_blocks, int32_t block_size,
+                                          nkv_dtype_t dtype, void* stream) {
+  if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  if (num_tokens < 0) return fail(NKV_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_kv_heads <= 0 || head_dim <= 0) return fail(NKV_ERR_INVALID_ARG, "num_kv_heads and head_dim must be positive");
+  if (num_blocks <= 0 || block_size <= 0) return fail(NKV_ERR_INVALID_ARG, "num_blocks and block_size must be positive");
+  if (int64_t(num_blocks) * block_size > int64_t(INT32_MAX))
+    return fail(NKV_ERR_UNSUPPORTED, "pool has more than 2^31-1 rows");
+  const int eb = elem_bytes(dtype);
+  const int64_t row = int64_t(num_kv_heads) * head_dim;
+  if ((row * eb) % 16 != 0)
+    return fail(NKV_ERR_UNSUPPORTED, "row of %lld elements is not a multiple of 16 bytes", (long long)row);
+  if (key_row_stride < row || value_row_stride < row)
+    return fail(NKV_ERR_INVALID_ARG, "row stride below num_kv_heads*head_dim");
+  if ((key_row_stride * eb) % 16 != 0 || (value_row_stride * eb) % 16 != 0)
+    return fail(NKV_ERR_INVALID_ARG, "row strides must be multiples of 16 bytes");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(NKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(NKV_ERR_INVALID_ARG, "key/value/cache pointers must be 16-byte aligned");
+  nkv::StoreArgs a{key, key_row_stride * eb, value, value_row_stride * eb, k_cache, v_cache,
+                   slot_mapping, num_tokens, row * eb, num_cus()};
+  return hip_status(nkv::launch_store(a, static_cast<hipStream_t>(stream)), "store launch");
+}
+
+NKV_EXPORT nkv_status_t nkv_paged_attn_prefill(
+    const void* q, int64_t q_row_stride, const void* k_cache, const void* v_cache,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_table,
+    int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+    int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks, int32_t block_size, float softmax_scale, nkv_dtype_t dtype, void* out,
+    void* stream) {
+  nkv::PrefillArgs a{};
+  nkv_status_t st = check_paged(k_cache, v_cache, block_table, max_blocks_per_seq, num_seqs,
+                                num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                                softmax_scale, dtype, &a.p);
+  if (st != NKV_OK) return st;
+  if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(NKV_ERR_INVALID_ARG, "negative size");
+  if (max_seqlen_q > max_seqlen_k)
+    return fail(NKV_ERR_INVALID_ARG, "max_seqlen_q (%d) > max_seqlen_k (%d)", max_seqlen_q, max_seqlen_k);
+  if (int64_t(max_seqlen_k) > int64_t(max_blocks_per_seq) * block_size)
+    return fail(NKV_ERR_INVALID_ARG, "max_seqlen_k exceeds max_blocks_per_seq*block_size");
+  const int64_t qrow = int64_t(num_q_heads) * head_dim;
+  if (q_row_stride < qrow) return fail(NKV_ERR_INVALID_ARG, "q_row_stride below num_q_heads*head_dim");
+  const int eb = elem_bytes(dtype);
+  if ((q_row_stride * eb) % 16 != 0) return fail(NKV_ERR_INVALID_ARG, "q_row_stride must be a multiple of 16 bytes");
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  if (!q || !out || !cu_seqlens_q || !cu_seqlens_k) return fail(NKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(q) || !aligned16(out)) return fail(NKV_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
+  a.q = q;
+  a.q_row_elems = q_row_stride;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.max_seqlen_q = max_seqlen_q;
+  a.max_seqlen_k = max_seqlen_k;
+  a.out = out;
+  return hip_status(nkv::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+NKV_EXPORT size_t nkv_paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                      int32_t num_kv_heads, int32_t head_dim,
+                                                      int32_t max_blocks_per_seq,
+                                                      int32_t block_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || block_size <= 0)
+    return 0;
+  return nkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          block_size, num_cus())
+      .workspace_bytes;
+}
+
+NKV_EXPORT nkv_status_t nkv_paged_attn_decode(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* context_lens,
+    const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+    float softmax_scale, nkv_dtype_t dtype, void* out, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  nkv::DecodeArgs a{};
+  nkv_status_t st = check_paged(k_cache, v_cache, block_table, max_blocks_per_seq, num_seqs,
+                                num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                                softmax_scale, dtype, &a.p);
+  if (st != NKV_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (!q || !out || !context_lens) return fail(NKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(q) || !aligned16(out)) return fail(NKV_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
+  const nkv::DecodePlan plan = nkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                max_blocks_per_seq, block_size, a.p.num_cus);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes)
+      return fail(NKV_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.workspace_bytes,
+                  workspace ? workspace_bytes : size_t(0));
+    if (!aligned16(workspace)) return fail(NKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  a.q = q;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.workspace = workspace;
+  return hip_status(nkv::launch_decode(a, plan, static_cast<hipStream_t>(stream)), "decode launch");
+}

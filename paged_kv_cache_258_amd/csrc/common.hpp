@@ -1,0 +1,81 @@
+// Shared device helpers for the nkv kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nkv {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+// log2(e): softmax is evaluated as exp2(x * scale * log2(e) - m).
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Storage tags.  A bf16 element is kept as its raw 16 bits.
+struct F32 {
+  using elem = float;
+  static constexpr int bytes = 4;
+};
+struct BF16 {
+  using elem = uint16_t;
+  static constexpr int bytes = 2;
+};
+
+// ---- bf16 <-> f32 --------------------------------------------------------------------
+// A bf16 is the top half of a binary32, so widening is a 16-bit shift of the pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---- cross-lane --------------------------------------------------------------------
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i inside each 8-lane half row
+constexpr int kDppRowRor8 = 0x128;       // lane i <- lane (i+8)%16 inside each 16-lane row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the 8 lanes of an aligned 8-lane group; every lane gets the total.
+__device__ __forceinline__ float group8_sum(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) {
+  int lane = __lane_id();
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+// exp2 that returns exactly 0 for -inf (hardware v_exp_f32 does).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int64_t row_of(const int32_t* __restrict__ table_row, int pos,
+                                          int log2_bs, int bs_mask) {
+  const int64_t phys = table_row[pos >> log2_bs];
+  return (phys << log2_bs) + (pos & bs_mask);
+}
+
+}  // namespace nkv

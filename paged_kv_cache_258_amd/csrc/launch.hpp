@@ -1,0 +1,78 @@
+// Host-side launch descriptors shared by the C ABI layer (api.hip) and the kernel
+// files.  The ABI layer validates arguments and fills these; the launchers only size
+// grids and enqueue kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nkv {
+
+enum class Dtype { F32 = 0, BF16 = 1 };
+
+struct StoreArgs {
+  const void* key;
+  int64_t key_row_bytes;
+  const void* value;
+  int64_t value_row_bytes;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slot_mapping;
+  int32_t num_tokens;
+  int64_t row_bytes;  // num_kv_heads * head_dim * element size
+  int num_cus;
+};
+
+struct PagedArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t log2_block_size;
+  float scale_log2e;  // softmax_scale * log2(e)
+  Dtype dtype;
+  int num_cus;
+};
+
+struct PrefillArgs {
+  PagedArgs p;
+  const void* q;
+  int64_t q_row_elems;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t max_seqlen_q;
+  int32_t max_seqlen_k;
+  void* out;
+};
+
+struct DecodeArgs {
+  PagedArgs p;
+  const void* q;
+  const int32_t* context_lens;
+  void* out;
+  void* workspace;
+};
+
+// Split-K plan of a decode call: each (sequence, KV head) is cut into chunks of
+// `split_tokens` logical positions; `max_splits` bounds the chunks of any sequence.
+struct DecodePlan {
+  int32_t split_tokens;
+  int32_t max_splits;
+  size_t workspace_bytes;
+};
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                       int num_cus);
+
+hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+}  // namespace nkv

@@ -1,0 +1,161 @@
+"""Decode parity: nkv_store_kvcache + nkv_paged_attn_decode against the oracle.
+
+The oracle stores the same new tokens into its own copy of the pool and runs
+decode_ref; the GPU side stores with its kernel and decodes.  Unwritten pool rows are
+NaN, so reading past a context length (or weighting such a row by zero) fails.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from paged_kv_cache_258_amd import nkv_paged_attn_decode, nkv_store_kvcache
+from paged_kv_cache_258_amd import workloads as wl
+
+from _gpu_helpers import assert_close, dev_i32, elem, host_bits, log, require_gpu, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_decode(case, seqs=None):
+    kb, vb = host_bits(case.k_cache), host_bits(case.v_cache)
+    if case.k is not None:
+        kb, vb = ref.store_ref(host_bits(case.k), host_bits(case.v), kb, vb, case.slot_mapping)
+    return ref.decode_ref(host_bits(case.q), kb, vb, case.context_lens, case.block_table,
+                          case.shape.scale, elem=elem(case.q), seqs=seqs)
+
+
+def gpu_decode(case, kc=None, vc=None, table=None):
+    dev = case.q.device
+    kc = case.k_cache.clone() if kc is None else kc
+    vc = case.v_cache.clone() if vc is None else vc
+    if case.k is not None:
+        nkv_store_kvcache(case.k, case.v, kc, vc, dev_i32(case.slot_mapping, dev))
+    out = nkv_paged_attn_decode(case.q, kc, vc, dev_i32(case.context_lens, dev),
+                                dev_i32(case.block_table if table is None else table, dev),
+                                case.shape.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def random_case(seed, lens, shape, bs_pad_blocks=1, extra_nan_block=False):
+    """Pool with NaN everywhere except the cached history; one new token per sequence."""
+    dev = require_gpu()
+    rng = np.random.default_rng(seed)
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    bs = shape.block_size
+    lens = np.asarray(lens, dtype=np.int32)
+    nblk = [wl.blocks_needed(l, bs) for l in lens]
+    maxb = max(nblk) + bs_pad_blocks
+    nb = sum(nblk) + 2
+    table = wl.assign_blocks(rng, nblk, nb, maxb)
+    pool_nb = nb + (1 if extra_nan_block else 0)
+    if extra_nan_block:
+        table[table < 0] = nb
+    kc = wl.nan_pool(pool_nb, bs, shape.num_kv_heads, shape.head_dim, shape.dtype, dev)
+    vc = wl.nan_pool(pool_nb, bs, shape.num_kv_heads, shape.head_dim, shape.dtype, dev)
+    hist = np.concatenate([wl.slots_for_positions(table[b], np.arange(l - 1), bs)
+                           for b, l in enumerate(lens)] + [np.zeros(0, np.int32)])
+    if len(hist):
+        wl._fill_cached(kc, gen, hist)
+        wl._fill_cached(vc, gen, hist)
+    b = len(lens)
+    q = wl.randn((b, shape.num_q_heads, shape.head_dim), gen, dev, shape.dtype)
+    k = wl.randn((b, shape.num_kv_heads, shape.head_dim), gen, dev, shape.dtype)
+    v = wl.randn((b, shape.num_kv_heads, shape.head_dim), gen, dev, shape.dtype)
+    slots = np.array([wl.slots_for_positions(table[i], [lens[i] - 1], bs)[0] for i in range(b)],
+                     dtype=np.int32)
+    return wl.DecodeCase("random", shape, q, k, v, slots, kc, vc, table, lens)
+
+
+def check(case, tag, seqs=None):
+    log(f"[decode] {tag}: B={len(case.context_lens)} shape={case.shape} "
+        f"lens[:8]={case.context_lens[:8].tolist()}")
+    got = to_f64(gpu_decode(case))
+    want = oracle_decode(case, seqs)
+    if seqs is not None:
+        got, want = got[list(seqs)], want[list(seqs)]
+    return assert_close(got, want, tag)
+
+
+def test_decode_c1_tiny_fp32_chain():
+    # store prefill tokens, then the decode tokens, then decode (store before read)
+    dev = require_gpu()
+    pre, dec = wl.c1_tiny(dev)
+    kc, vc = pre.k_cache.clone(), pre.v_cache.clone()
+    nkv_store_kvcache(pre.k, pre.v, kc, vc, dev_i32(pre.slot_mapping, dev))
+    kb, vb = ref.store_ref(host_bits(pre.k), host_bits(pre.v), host_bits(pre.k_cache),
+                           host_bits(pre.v_cache), pre.slot_mapping)
+    dec.k_cache, dec.v_cache = kc, vc
+    got = to_f64(gpu_decode(dec, kc=kc, vc=vc))
+    kb, vb = ref.store_ref(host_bits(dec.k), host_bits(dec.v), kb, vb, dec.slot_mapping)
+    want = ref.decode_ref(host_bits(dec.q), kb, vb, dec.context_lens, dec.block_table,
+                          dec.shape.scale, elem="f32")
+    mx, _ = assert_close(got, want, "C1 decode (fp32)")
+    log(f"  C1 fp32 max error {mx:.3e} (information: expected about 1e-6)")
+    assert mx < 1e-4
+
+
+def test_decode_c2_full():
+    dev = require_gpu()
+    case = wl.c2_decode(dev)
+    check(case, "C2 64 seqs, L in [512,4096]")
+
+
+def test_decode_c2_nan_padded_table():
+    dev = require_gpu()
+    case = wl.c2_decode(dev, batch=8, extra_nan_block=True)
+    check(case, "C2 table padded with a NaN block")
+
+
+EDGE_LENS = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 255, 256, 257, 511, 1000, 1023, 1024,
+             1025, 4096, 5000]
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,dtype", [
+    (32, 8, 128, 256, "bf16"),
+    (32, 8, 128, 16, "bf16"),
+    (8, 8, 128, 64, "bf16"),
+    (16, 8, 128, 32, "bf16"),
+    (64, 8, 128, 256, "bf16"),
+    (16, 4, 64, 16, "bf16"),
+    (4, 1, 64, 16, "f32"),
+    (16, 2, 128, 128, "f32"),
+])
+def test_decode_edge_lengths(hq, hkv, d, bs, dtype):
+    shape = wl.Shape(hq, hkv, d, bs, dtype)
+    case = random_case(100 + hq + d + bs, EDGE_LENS, shape)
+    check(case, f"edge lengths {shape}")
+
+
+@pytest.mark.parametrize("split", ["64", "128", "512"])
+def test_decode_forced_splits(split, monkeypatch):
+    monkeypatch.setenv("NKV_DECODE_SPLIT_TOKENS", split)
+    shape = wl.QWEN3_8B
+    case = random_case(200, [1, 63, 64, 65, 300, 777, 2048, 3001], shape)
+    check(case, f"split_tokens={split}")
+
+
+def test_decode_deterministic_and_block_permutation_invariant():
+    dev = require_gpu()
+    case = random_case(300, [70, 900, 2500, 4096, 33], wl.QWEN3_8B)
+    out1 = gpu_decode(case)
+    out2 = gpu_decode(case)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), "not bitwise reproducible"
+    nb = case.k_cache.shape[0]
+    perm = torch.as_tensor(np.random.default_rng(301).permutation(nb), device=dev)
+    kc2 = torch.empty_like(case.k_cache)
+    vc2 = torch.empty_like(case.v_cache)
+    kc2[perm] = case.k_cache
+    vc2[perm] = case.v_cache
+    pn = perm.cpu().numpy()
+    table2 = np.where(case.block_table >= 0, pn[np.maximum(case.block_table, 0)], -1).astype(np.int32)
+    slots2 = (pn[case.slot_mapping // 256] * 256 + case.slot_mapping % 256).astype(np.int32)
+    case2 = wl.DecodeCase("perm", case.shape, case.q, case.k, case.v, slots2, kc2, vc2, table2,
+                          case.context_lens)
+    out3 = gpu_decode(case2)
+    assert torch.equal(out1.view(torch.int16), out3.view(torch.int16)), \
+        "output changed under a physical block permutation"
