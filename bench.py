@@ -1,0 +1,297 @@
+"""Benchmark of the paged KV-cache data plane on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input:
+  * headline (decode): Qwen3-8B-shaped single-layer decode, 64 sequences with context
+    lengths uniform in [512, 4096], block_size 256: store the 64 new tokens' K/V through
+    slot_mapping, then paged decode attention over the pool.  Inputs are already in HBM;
+    three copies of the pool at different addresses are rotated so consecutive steps do
+    not hit the 256 MB last-level cache with the previous step's K/V.
+  * prefill legs (reported beside it): 8 x 2048-token causal varlen prefill (store all
+    16384 tokens, then attend through the block tables) and the prefix-cached chunked
+    prefill (16 sequences, shared 1024-token prefix, 512-token chunks).
+
+value = algorithmic bytes of the decode step (store + decode) / measured step time.
+roofline = the decode call (split kernel + its reduce) timed with HIP events on the
+stream it runs on: algorithmic decode bytes / average duration vs 8 TB/s.
+cpu_baseline = the float64 CPU oracle (store_ref + decode_ref) on the same C2 batch.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-prefill]
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "paged_kv_cache_258_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def i32(a, dev):
+    import numpy as np
+    import torch
+    return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32), device=dev)
+
+
+def bench_decode(dev, steps, warmup):
+    import torch
+    import paged_kv_cache_258_amd as nkv
+    from paged_kv_cache_258_amd import accounting as acc
+    from paged_kv_cache_258_amd import workloads as wl
+
+    case = wl.c2_decode(dev)
+    sh = case.shape
+    lens_d = i32(case.context_lens, dev)
+    table_d = i32(case.block_table, dev)
+    slots_d = i32(case.slot_mapping, dev)
+    sets = [(case.k_cache, case.v_cache)] + [(case.k_cache.clone(), case.v_cache.clone())
+                                            for _ in range(2)]
+    out = torch.empty_like(case.q)
+    need = nkv.nkv_paged_attn_decode_workspace_size(len(case.context_lens), sh.num_q_heads,
+                                                    sh.num_kv_heads, sh.head_dim,
+                                                    case.block_table.shape[1], sh.block_size)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        kc, vc = sets[i % 3]
+        if ev is not None:
+            ev[0].record()
+        nkv.nkv_store_kvcache(case.k, case.v, kc, vc, slots_d)
+        if ev is not None:
+            ev[1].record()
+        nkv.nkv_paged_attn_decode(case.q, kc, vc, lens_d, table_d, sh.scale, out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step(i, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / steps
+    store_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    dec_bytes = acc.decode_bytes(case.context_lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
+                                 sh.block_size, sh.elem_bytes)
+    st_bytes = acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
+    log(f"[decode C2] step {ms_step*1e3:.1f} us (store {store_ms*1e3:.1f} us, decode "
+        f"{dec_ms*1e3:.1f} us) -> decode {dec_bytes/dec_ms/1e6:.0f} GB/s, wall {wall:.3f}s")
+    return dict(case=case, ms_step=ms_step, store_ms=store_ms, dec_ms=dec_ms, dec_bytes=dec_bytes,
+                st_bytes=st_bytes, workspace_bytes=need)
+
+
+def bench_prefill(dev, which, steps, warmup):
+    import torch
+    import paged_kv_cache_258_amd as nkv
+    from paged_kv_cache_258_amd import accounting as acc
+    from paged_kv_cache_258_amd import workloads as wl
+
+    prefix = None
+    if which == "C3":
+        case = wl.c3_prefill(dev)
+    else:
+        prefix, case = wl.c4_prefix_chunk(dev)
+    sh = case.shape
+    kc, vc = case.k_cache, case.v_cache
+    if prefix is not None:
+        pk, pv, ps = prefix
+        nkv.nkv_store_kvcache(pk, pv, kc, vc, i32(ps, dev))
+    cu_q, cu_k = i32(case.cu_seqlens_q, dev), i32(case.cu_seqlens_k, dev)
+    table, slots = i32(case.block_table, dev), i32(case.slot_mapping, dev)
+    out = torch.empty_like(case.q)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        nkv.nkv_store_kvcache(case.k, case.v, kc, vc, slots)
+        if ev is not None:
+            ev[1].record()
+        nkv.nkv_paged_attn_prefill(case.q, kc, vc, cu_q, cu_k, table, case.max_seqlen_q,
+                                   case.max_seqlen_k, sh.scale, out=out)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    store_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    pf_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    flops = acc.prefill_flops(case.cu_seqlens_q, case.cu_seqlens_k, sh.num_q_heads, sh.head_dim)
+    st_bytes = acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
+    tflops = flops / pf_ms / 1e9
+    log(f"[prefill {which}] store {store_ms*1e3:.1f} us ({st_bytes/store_ms/1e6:.0f} GB/s), "
+        f"prefill {pf_ms*1e3:.1f} us -> {tflops:.1f} TFLOP/s")
+    return {"workload": which, "prefill_us": round(pf_ms * 1e3, 2),
+            "tflops": round(tflops, 2), "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flop": flops, "store_us": round(store_ms * 1e3, 2),
+            "store_gbs": round(st_bytes / store_ms / 1e6, 1)}
+
+
+def cpu_baseline(case, budget_s=10.0):
+    """The float64 oracle (store_ref + decode_ref) on the full C2 batch, on host cores."""
+    import numpy as np
+    import torch
+    from oracle import ref
+    from paged_kv_cache_258_amd import accounting as acc
+
+    def bits(t):
+        return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    t_copy = time.perf_counter()
+    q, k, v = bits(case.q), bits(case.k), bits(case.v)
+    kc, vc = bits(case.k_cache), bits(case.v_cache)
+    t_copy = time.perf_counter() - t_copy
+    sh = case.shape
+    runs, t_tot = 0, 0.0
+    while runs == 0 or (t_tot < budget_s and runs < 20):
+        t = time.perf_counter()
+        kb, vb = ref.store_ref(k, v, kc, vc, case.slot_mapping)
+        ref.decode_ref(q, kb, vb, case.context_lens, case.block_table, sh.scale, elem="bf16")
+        t_tot += time.perf_counter() - t
+        runs += 1
+    per = t_tot / runs
+    nbytes = acc.decode_bytes(case.context_lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
+                              sh.block_size, sh.elem_bytes) + \
+        acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
+    try:
+        import threadpoolctl
+        blas = [p["num_threads"] for p in threadpoolctl.threadpool_info() if p["user_api"] == "blas"]
+        threads = max(blas) if blas else 1
+    except Exception:  # noqa: BLE001
+        threads = 1
+    log(f"[cpu oracle] {per:.3f} s per C2 step ({runs} runs), D2H copy {t_copy:.2f}s")
+    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"full C2 batch (64 seqs, sum ctx {int(case.context_lens.sum())}): "
+                      f"store_ref + decode_ref in numpy float64, {runs} run(s), "
+                      f"{per:.2f} s each; host affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def traffic_from_counters(kernel_sha):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; otherwise None."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha") != kernel_sha:
+        return None
+    return c.get("hbm_bytes_per_decode_call")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill legs")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the data plane shards by KV head; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_258_amd as nkv
+
+    nkv.load()
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs")
+
+    torch.cuda.synchronize()
+    d = bench_decode(dev, args.steps, args.warmup)
+    prefill = []
+    if not args.no_prefill:
+        prefill.append(bench_prefill(dev, "C3", max(5, args.steps // 2), 2))
+        prefill.append(bench_prefill(dev, "C4", max(5, args.steps // 2), 2))
+    cpu = None if args.no_cpu else cpu_baseline(d["case"])
+
+    step_bytes = d["dec_bytes"] + d["st_bytes"]
+    value = step_bytes / d["ms_step"] / 1e6
+    achieved = d["dec_bytes"] / d["dec_ms"] / 1e6
+    sha = kernel_source_sha(["decode.hip", "common.hpp", "launch.hpp"])
+    case = d["case"]
+    line = {
+        "metric": "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% MFMA peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "C2 Qwen3-8B-shaped single-layer paged decode step (store 64 new "
+                        "tokens + decode): 64 seqs, context U[512,4096], 32 Q / 8 KV heads, "
+                        "head_dim 128, block_size 256, bf16",
+            "num_seqs": len(case.context_lens),
+            "sum_context_tokens": int(case.context_lens.sum()),
+            "num_blocks": int(case.k_cache.shape[0]),
+            "step_bytes": int(step_bytes),
+            "pool_copies_rotated": 3,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "nkv_paged_attn_decode (decode_split_kernel + decode_reduce_kernel)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_counters(sha),
+            "algorithmic_bytes_per_launch": int(d["dec_bytes"]),
+            "avg_launch_us": round(d["dec_ms"] * 1e3, 2),
+            "kernel_source_sha": sha,
+        },
+        "store": {"avg_launch_us": round(d["store_ms"] * 1e3, 2),
+                  "gbs": round(d["st_bytes"] / d["store_ms"] / 1e6, 1)},
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
