@@ -275,7 +275,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "nkv_paged_attn_decode (decode_split_kernel + decode_reduce_kernel)",
+            "kernel": "nkv_paged_attn_decode (decode_streamk_kernel + decode_fixup_kernel)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -13,7 +13,8 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnkv.so")
+LIB_PATH = os.environ.get("NKV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libnkv.so")
 
 NKV_OK, NKV_ERR_INVALID_ARG, NKV_ERR_UNSUPPORTED, NKV_ERR_WORKSPACE, NKV_ERR_HIP = range(5)
 NKV_F32, NKV_BF16 = 0, 1

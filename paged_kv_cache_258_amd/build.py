@@ -48,24 +48,28 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BUILD) -> str:
+    """Compile every HIP source and link ``out``; ``defines`` are extra -D flags."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     objs, cmds = [], []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
         for r in ex.map(_run, cmds):
-            if verbose and r.stderr:
-                print(r.stderr, file=sys.stderr)
-    tmp = LIB + ".tmp"
+            noise = ("packed-fp32-ops", "warning: argument unused")
+            msg = "\n".join(l for l in r.stderr.splitlines() if l.strip() and not any(n in l for n in noise))
+            if verbose and msg:
+                print(msg, file=sys.stderr)
+    tmp = out + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -64,6 +64,54 @@ __device__ __forceinline__ float group8_sum(float x) {
   return x;
 }
 
+// Sum / max with the lane 16 (resp. 32) positions away, every lane getting the result:
+// v_permlane16_swap / v_permlane32_swap (gfx950) swap rows (halves) between two VGPRs,
+// so swapping a value with itself yields both partners' values in the two outputs.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.  Used
+// for loads that write LDS directly (global_load_lds), which the compiler does not
+// track; the "memory" clobber keeps LDS reads from moving above the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Global -> LDS copies (global_load_lds, 16 or 4 bytes per lane; lane i writes
+// lds_base + i*size, lds_base the same for the whole wave).  They are issued through
+// inline asm so that the compiler neither tracks them nor guards every later LDS read
+// with a "wait for all vector loads": each caller orders them itself with wait_vmcnt.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p)));
+}
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
+  uint32_t saved;  // m0 is reserved by the compiler: restore it before leaving the asm
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(gptr), "s"(lds_addr(lds_base)) : "memory");
+}
+__device__ __forceinline__ void load_lds4(const void* gptr, void* lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(gptr), "s"(lds_addr(lds_base)) : "memory");
+}
+
 __device__ __forceinline__ float shfl_xor(float x, int mask) {
   int lane = __lane_id();
   return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));

@@ -59,11 +59,17 @@ struct DecodeArgs {
   void* workspace;
 };
 
-// Split-K plan of a decode call: each (sequence, KV head) is cut into chunks of
-// `split_tokens` logical positions; `max_splits` bounds the chunks of any sequence.
+// Work plan of a decode call.
+//   fp32 (split-K): each (sequence, KV head) is cut into chunks of `split_tokens`
+//   logical positions; `max_splits` bounds the chunks of any sequence.
+//   bf16 (stream-K): `wgs` persistent workgroups share the batch's rounds equally;
+//   sequences are processed `seq_chunk` at a time.
+// `workspace_bytes` covers whichever path the dtype selects.
 struct DecodePlan {
   int32_t split_tokens;
   int32_t max_splits;
+  int32_t wgs;
+  int32_t seq_chunk;
   size_t workspace_bytes;
 };
 
