@@ -10,7 +10,7 @@
 
 #include <mutex>
 
-#include "../../include/nkv.h"
+#include "nkv.h"  // include/ is on the include path
 #include "launch.hpp"
 
 #define NKV_EXPORT extern "C" __attribute__((visibility("default")))

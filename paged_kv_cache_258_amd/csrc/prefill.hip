@@ -7,19 +7,27 @@
 // block_table=...)).  Query i of a segment with Lq queries and Lk keys sits at position
 // Lk - Lq + i and sees keys j <= Lk - Lq + i.
 //
-// bf16 path (dense contraction -> MFMA, v_mfma_f32_32x32x16_bf16 on gfx950):
-//   grid (seq * kv_head, q-tile) with q-tiles dispatched longest-first; one workgroup
-//   holds the G query heads of one KV head for BQ queries: max(G,4) waves, each wave
-//   32 queries of one head.  K/V tiles of 64 keys are gathered through the block table
-//   into LDS once and used by all waves (every head of the GQA group and every query
-//   sub-tile), K row-major, V transposed (dims x keys) so both MFMA operands are
-//   16-byte LDS reads.  Scores are computed transposed, S^T = K Q^T, so each lane owns
-//   one query: the row max needs one cross-half exchange and the row sum stays in the
-//   lane until the end.  P goes from the S^T accumulator registers straight into the
-//   B operand of O^T += V^T P^T (the key order inside each 16-key step is permuted the
-//   same way on both operands, so no shuffle is needed).  The running max is raised
-//   lazily (rescale only past 2^8 headroom).  Only tiles that cross the causal
-//   diagonal or the end of the keys apply the mask.
+// bf16 path (dense contraction -> MFMA, v_mfma_f32_32x32x16_bf16):
+//   grid (seq * kv_head, q-tile), q-tiles dispatched longest-first.  A workgroup holds
+//   the G query heads of one KV head; each wave owns 64 queries of one head (two
+//   32-query MFMA column blocks), so every K or V fragment read from LDS feeds two
+//   MFMAs.  K/V tiles of 64 keys are gathered through the block table into a double
+//   buffered LDS stage shared by all waves: K rows are copied HBM -> LDS directly
+//   (global_load_lds, chunk c of row t at c ^ t to spread banks); V is loaded to
+//   registers and written transposed (dims x keys, key order permuted to match the
+//   accumulator layout of S^T), so both MFMA operands are 16-byte LDS reads.  The next
+//   tile's copies are in flight while the current tile is computed.
+//   Scores are computed transposed, S^T = K Q^T, so each lane owns one query: its row
+//   max needs one exchange with the lane 32 away, its row sum stays in the lane.  P goes
+//   from the S^T accumulators straight into the B operand of O^T += V^T P^T.  A tile is
+//   processed as two 32-key halves, each QK -> softmax -> PV in turn: holding both halves'
+//   scores at once does not fit the register file next to the O^T accumulators (it spills
+//   and runs ~1.4x slower), and the four waves of a CU interleave one another's MFMA and
+//   softmax phases anyway.  The softmax uses one
+//   FMA + exp2 per score (scale folded in), the running max is raised lazily (rescale
+//   only past 2^8 headroom), and the row sum is a dot2 of the rounded bf16 weights.
+//   Only tiles that cross the causal diagonal or the end of the keys are masked.  The
+//   output goes through LDS so each row is written as one contiguous run.
 // fp32 path: a plain VALU kernel (one lane per query and head, online softmax), used
 //   for correctness-sized fp32 inputs.
 #include <math.h>
@@ -31,30 +39,33 @@ namespace nkv {
 
 constexpr int kBK = 64;                 // keys per tile
 constexpr float kLazy = 8.0f;           // log2 headroom before rescaling
-constexpr int kKPad = 8;                // bf16 elements of padding per K row in LDS
 constexpr int kVPad = 8;                // bf16 elements of padding per Vt row in LDS
 
 template <int D, int G>
 struct PfGeom {
-  static constexpr int NW = G > 4 ? G : 4;   // waves per workgroup
+  static constexpr int NW = G > 4 ? G : 4;      // waves per workgroup
   static constexpr int NT = NW * kWave;
-  static constexpr int QSUB = NW / G;        // 32-query sub-tiles per workgroup
-  static constexpr int BQ = 32 * QSUB;       // queries per workgroup
-  static constexpr int KS = D / 16;          // k-steps of the QK^T MFMA
-  static constexpr int DT = D / 32;          // 32-dim tiles of O^T
-  static constexpr int KROW = D + kKPad;     // LDS K row stride (elements)
-  static constexpr int VROW = kBK + kVPad;   // LDS Vt row stride (elements)
-  static constexpr int KCH = D / 8;          // 16-byte chunks per K row
-  static constexpr int K_LOADS = kBK * KCH / NT;            // per thread
-  static constexpr int V_QUADS = (kBK / 4) * KCH;          // (key quad, chunk) items
-  static constexpr int V_LOADS = (V_QUADS + NT - 1) / NT;   // per thread
-  static_assert(kBK * KCH % NT == 0, "K tile must split evenly over threads");
+  static constexpr int QSUB = NW / G;           // 64-query sub-tiles per workgroup
+  static constexpr int BQ = 64 * QSUB;          // queries per workgroup
+  static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
+  static constexpr int DT = D / 32;             // 32-dim tiles of O^T
+  static constexpr int CPR = D / 8;             // 16-byte chunks per K row
+  static constexpr int K_BYTES = kBK * D * 2;   // one K tile
+  static constexpr int VROW = kBK + kVPad;      // Vt row stride (elements)
+  static constexpr int VT_BYTES = D * VROW * 2;
+  static constexpr int STAGE = K_BYTES + VT_BYTES;
+  static constexpr int K_DMA = K_BYTES / 1024 / NW;   // K copy instructions per wave per tile
+  static constexpr int V_ITEMS = (kBK / 4) * CPR;     // (key quad, chunk) items per tile
+  static constexpr int OROW = D * 2 + 8;              // output staging row stride (bytes)
+  static_assert(K_BYTES % (1024 * NW) == 0, "K tile must split evenly over the waves");
+  static_assert(V_ITEMS <= NT, "one V item per thread");
+  static constexpr int SMEM = 2 * STAGE > NW * 64 * OROW ? 2 * STAGE : NW * 64 * OROW;
 };
 
-// Position of key k (0..63) of a tile inside the transposed V rows: within every
-// 16-key step, bits 2 and 3 of the key index are swapped.  This matches the order in
-// which the S^T accumulator of a 32x32 MFMA hands its keys to the PV step.
-__device__ __forceinline__ int vt_quad_pos(int kq) {  // kq = key / 4
+// Position of key quad kq (keys 4kq..4kq+3) of a tile inside the transposed V rows:
+// within every 16-key step, bits 2 and 3 of the key index are swapped, which is the
+// order in which a 32x32 MFMA accumulator of S^T hands its keys to the P.V step.
+__device__ __forceinline__ int vt_quad_pos(int kq) {
   return (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
 }
 
@@ -67,11 +78,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     int32_t num_kv_heads, int32_t log2_bs, float scale_log2e,
                     uint16_t* __restrict__ out) {
   using Geo = PfGeom<D, G>;
-  constexpr int NT = Geo::NT, KS = Geo::KS, DT = Geo::DT;
-  constexpr int KROW = Geo::KROW, VROW = Geo::VROW, KCH = Geo::KCH;
-
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kBK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VROW];
+  constexpr int NT = Geo::NT, KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, VROW = Geo::VROW;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Geo::SMEM];
 
   const int pair = blockIdx.x;
   const int b = pair / num_kv_heads;
@@ -87,190 +95,232 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = wave % G;
-  const int qs = wave / G;
-  const int h = g * G + hl;
+  const int h = g * G + wave % G;
   const int hq = G * num_kv_heads;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int wq0 = q0 + qs * 32;                       // this wave's first query
-  const int qi = wq0 + l32;                           // this lane's query
-
+  const int wq0 = q0 + (wave / G) * 64;               // this wave's first query
   const int kend = diag + min(q0 + Geo::BQ, lq);      // keys the workgroup needs
   const int ntiles = (kend + kBK - 1) / kBK;
-  const int wkend = wq0 < lq ? diag + min(wq0 + 32, lq) : 0;  // keys this wave needs
+  const int wkend = wq0 < lq ? diag + min(wq0 + 64, lq) : 0;   // keys this wave needs
   const int32_t* __restrict__ trow = block_table + int64_t(b) * max_blocks;
   const int bs_mask = (1 << log2_bs) - 1;
   const int64_t row_elems = int64_t(num_kv_heads) * D;
   const uint16_t* kbase = k_cache + int64_t(g) * D;
   const uint16_t* vbase = v_cache + int64_t(g) * D;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): 8 dims per lane per k-step ----
-  bf16x8_t qf[KS];
-  {
-    const bool ok = qi < lq && wq0 < lq;
-    const uint16_t* qp = q + int64_t(qstart + qi) * q_row + int64_t(h) * D + 8 * hh;
+  // ---- Q fragments (B operand of S^T = K Q^T): two 32-query blocks, 8 dims per lane ----
+  bf16x8_t qf[2][KS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = wq0 + qb * 32 + l32;
+    const bool ok = qi < lq;
+    const uint16_t* qp = q + int64_t(qstart + (ok ? qi : 0)) * q_row + int64_t(h) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+      const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
+      qf[qb][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
-  f32x16_t o[DT];
+  // ---- tile copies: K rows by DMA (this wave's share), V (one item per thread) to regs ----
+  int k_row[Geo::K_DMA], k_elem[Geo::K_DMA];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-
-  // ---- global -> register prefetch of one K/V tile ----
-  u32x4_t kreg[Geo::K_LOADS];
-  u32x4_t vreg[Geo::V_LOADS][4];
-
-  auto key_off = [&](int key) -> int64_t {  // element offset of (key, head g) row
+  for (int j = 0; j < Geo::K_DMA; ++j) {
+    const int s = (wave * Geo::K_DMA + j) * 64 + lane;   // LDS slot this lane fills
+    k_row[j] = s / CPR;
+    k_elem[j] = ((s % CPR) ^ (k_row[j] & (CPR - 1))) * 8;
+  }
+  const bool v_item = tid < Geo::V_ITEMS;
+  const int v_kq = tid % 16, v_c = tid / 16;
+  auto row_off = [&](int key) -> int64_t {          // element offset of (key, head g)
     const int64_t phys = trow[key >> log2_bs];
     return ((phys << log2_bs) + (key & bs_mask)) * row_elems;
   };
-
-  auto prefetch = [&](int kt) {
-    const int k0 = kt * kBK;
+  auto issue_k = [&](int t) {
+    uint8_t* sk = smem + (t & 1) * Geo::STAGE;
 #pragma unroll
-    for (int i = 0; i < Geo::K_LOADS; ++i) {
-      const int idx = tid + i * NT;
-      const int key = idx / KCH, c = idx % KCH;
-      const int ka = k0 + key;
-      kreg[i] = ka < lk ? *reinterpret_cast<const u32x4_t*>(kbase + key_off(ka) + c * 8)
-                        : u32x4_t{0, 0, 0, 0};
+    for (int j = 0; j < Geo::K_DMA; ++j) {
+      const int key = min(t * kBK + k_row[j], lk - 1);
+      load_lds16(kbase + row_off(key) + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
     }
+  };
+  u32x4_t vreg[4];
+  auto load_v = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < Geo::V_LOADS; ++i) {
-      const int idx = tid + i * NT;
-      const int kq = idx % 16, c = idx / 16;
+    for (int j = 0; j < 4; ++j) {
+      const int key = t * kBK + 4 * v_kq + j;
+      vreg[j] = (v_item && key < lk)
+                    ? *reinterpret_cast<const u32x4_t*>(vbase + row_off(key) + v_c * 8)
+                    : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto commit_v = [&](int t) {
+    if (!v_item) return;
+    uint16_t* vt = reinterpret_cast<uint16_t*>(smem + (t & 1) * Geo::STAGE + Geo::K_BYTES);
+    const int pos = 4 * vt_quad_pos(v_kq);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ka = k0 + 4 * kq + j;
-        vreg[i][j] = (idx < Geo::V_QUADS && ka < lk)
-                         ? *reinterpret_cast<const u32x4_t*>(vbase + key_off(ka) + c * 8)
-                         : u32x4_t{0, 0, 0, 0};
-      }
+    for (int w = 0; w < 4; ++w) {       // dims 2w, 2w+1 of this chunk: 4 keys each
+      const uint32_t a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
+      const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+      const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+      *reinterpret_cast<u32x2_t*>(&vt[(v_c * 8 + 2 * w) * VROW + pos]) = lo;
+      *reinterpret_cast<u32x2_t*>(&vt[(v_c * 8 + 2 * w + 1) * VROW + pos]) = hi;
     }
   };
 
-  auto commit = [&]() {
+  f32x16_t o[2][DT];
 #pragma unroll
-    for (int i = 0; i < Geo::K_LOADS; ++i) {
-      const int idx = tid + i * NT;
-      const int key = idx / KCH, c = idx % KCH;
-      *reinterpret_cast<u32x4_t*>(&s_k[key * KROW + c * 8]) = kreg[i];
-    }
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int i = 0; i < Geo::V_LOADS; ++i) {
-      const int idx = tid + i * NT;
-      if (idx >= Geo::V_QUADS) continue;
-      const int kq = idx % 16, c = idx / 16;
-      const int pos = 4 * vt_quad_pos(kq);
-      // 4 keys x 8 dims -> for each dim, its 4 keys as two packed bf16 pairs
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = vreg[i][0][w], a1 = vreg[i][1][w];
-        const uint32_t a2 = vreg[i][2][w], a3 = vreg[i][3][w];
-        const u32x2_t lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        const u32x2_t hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        *reinterpret_cast<u32x2_t*>(&s_vt[(c * 8 + 2 * w) * VROW + pos]) = lo;
-        *reinterpret_cast<u32x2_t*>(&s_vt[(c * 8 + 2 * w + 1) * VROW + pos]) = hi;
-      }
+      for (int r = 0; r < 16; ++r) o[qb][dt][r] = 0.f;
+  float m[2] = {-INFINITY, -INFINITY};
+  float lsum[2] = {0.f, 0.f};
+  const uint32_t ones = 0x3f803f80u;   // bf16 pair (1, 1)
+
+  // S^T for one 32-key half of the tile in stage `sk`
+  auto qk = [&](const uint8_t* sk, int kb, f32x16_t (&s)[2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
+    const int t = kb * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+          sk + (t * CPR + ((2 * ks + hh) ^ (t & (CPR - 1)))) * 16);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb], 0, 0, 0);
     }
   };
-
-  prefetch(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();                                   // previous tile fully consumed
-    commit();
-    __syncthreads();
-    if (kt + 1 < ntiles) prefetch(kt + 1);
-    const int k0 = kt * kBK;
-    if (k0 >= wkend) continue;                         // this wave is past its keys
-
-    // ---- S^T = K Q^T for the two 32-key halves of the tile ----
-    f32x16_t s[2];
+  // softmax of one half: mask (if needed), lazy max, P as bf16 in P.V key order.
+  // Masked halves are scaled before the mask is applied (cs = 1 afterwards) so that a
+  // zero softmax_scale cannot turn -inf into NaN; unmasked halves fold the scale into
+  // the exponent's FMA.
+  auto softmax = [&](f32x16_t (&s)[2], int k0h, bf16x8_t (&pf)[2][2]) {
+    const bool masked = (k0h + 31 > diag + wq0) || (k0h + 32 > lk);
+    const float cs = masked ? 1.0f : scale_log2e;
+    float mx[2];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
+    for (int qb = 0; qb < 2; ++qb) {
+      if (masked) {
+        const int qi = wq0 + qb * 32 + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[t2][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            &s_k[(t2 * 32 + l32) * KROW + ks * 16 + 8 * hh]);
-        s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[t2], 0, 0, 0);
-      }
-    }
-
-    // ---- scale, mask (diagonal / tail tiles only), running max ----
-    const bool masked = (k0 + kBK - 1 > diag + wq0) || (k0 + kBK > lk);
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[t2][r] * scale_log2e;
-        if (masked) {
-          const int key = k0 + t2 * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          x = (key < lk && key <= diag + qi) ? x : -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0h + 8 * (r >> 2) + 4 * hh + (r & 3);
+          s[qb][r] = (key < lk && key <= diag + qi) ? s[qb][r] * scale_log2e : -INFINITY;
         }
-        s[t2][r] = x;
-        mloc = fmaxf(mloc, x);
       }
-    mloc = fmaxf(mloc, shfl_xor(mloc, 32));
-    if (__any(mloc > m_run + kLazy)) {
-      const float mn = fmaxf(m_run, mloc);
-      const float alpha = fast_exp2(m_run - mn);
-      l_part *= alpha;
+      float x = s[qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[qb][r]);
+      mx[qb] = xor32_max(x) * cs;
+    }
+    if (__any(mx[0] > m[0] + kLazy || mx[1] > m[1] + kLazy)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mn = fmaxf(m[qb], mx[qb]);
+        const float alpha = fast_exp2(m[qb] - mn);
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha;
+        m[qb] = mn;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4_t w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = fast_exp2(fmaf(s[qb][8 * kk + 2 * i], cs, -m[qb]));
+          const float p1 = fast_exp2(fmaf(s[qb][8 * kk + 2 * i + 1], cs, -m[qb]));
+          w[i] = pack_bf16x2(p0, p1);
+          lsum[qb] = dot2_bf16(w[i], ones, lsum[qb]);
+        }
+        pf[qb][kk] = __builtin_bit_cast(bf16x8_t, w);
+      }
+  };
+  auto pv = [&](const uint8_t* sv, int kb, const bf16x8_t (&pf)[2][2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            sv + ((dt * 32 + l32) * VROW + kb * 32 + kk * 16 + 8 * hh) * 2);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kk], o[qb][dt], 0, 0, 0);
+      }
+  };
+
+  // ---- prologue: tile 0 into stage 0 ----
+  issue_k(0);
+  load_v(0);
+  commit_v(0);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) {                                   // next tile's copies fly during this one
+      issue_k(t + 1);
+      load_v(t + 1);
+    }
+    const int k0 = t * kBK;
+    if (k0 < wkend) {
+      const uint8_t* sk = smem + (t & 1) * Geo::STAGE;
+      const uint8_t* sv = sk + Geo::K_BYTES;
+      f32x16_t s0[2], s1[2];
+      bf16x8_t p0[2][2], p1[2][2];
+      qk(sk, 0, s0);
+      softmax(s0, k0, p0);
+      pv(sv, 0, p0);
+      if (k0 + 32 < wkend) {
+        qk(sk, 1, s1);
+        softmax(s1, k0 + 32, p1);
+        pv(sv, 1, p1);
+      }
+    }
+    if (more) commit_v(t + 1);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  // ---- epilogue: O^T / l -> bf16 rows staged in LDS, then contiguous row writes ----
+  uint8_t* ost = smem + wave * 64 * Geo::OROW;
+  if (wq0 < lq) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float inv = 1.0f / xor32_sum(lsum[qb]);   // the two lane halves hold different keys
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      m_run = mn;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = dt * 32 + 8 * r4 + 4 * hh;
+          const u32x2_t w = {pack_bf16x2(o[qb][dt][4 * r4 + 0] * inv, o[qb][dt][4 * r4 + 1] * inv),
+                             pack_bf16x2(o[qb][dt][4 * r4 + 2] * inv, o[qb][dt][4 * r4 + 3] * inv)};
+          *reinterpret_cast<u32x2_t*>(ost + (qb * 32 + l32) * Geo::OROW + d0 * 2) = w;
+        }
     }
-
-    // ---- P = exp2(S - m), packed to bf16 in PV k-step order ----
-    bf16x8_t pf[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int mm = 0; mm < 8; ++mm) {
-        const float p = fast_exp2(s[kk >> 1][8 * (kk & 1) + mm] - m_run);
-        l_part += p;
-        pf[kk][mm] = (__bf16)p;
-      }
-    }
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            &s_vt[(dt * 32 + l32) * VROW + kk * 16 + 8 * hh]);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[dt], 0, 0, 0);
-      }
   }
-
-  // ---- epilogue: O / l -> bf16 ----
-  const float l_tot = l_part + shfl_xor(l_part, 32);
-  if (qi < lq && wq0 < lq) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* op = out + (int64_t(qstart + qi) * hq + h) * D;
+  __syncthreads();
+  if (wq0 < lq) {
+    constexpr int RPI = 64 / CPR;                 // rows per 64-lane pass
+    const int rr = lane / CPR, cc = lane % CPR;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = dt * 32 + 8 * r4 + 4 * hh;
-        const u32x2_t w = {pack_bf16x2(o[dt][4 * r4 + 0] * inv, o[dt][4 * r4 + 1] * inv),
-                           pack_bf16x2(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(op + d0) = w;
+    for (int i = 0; i < 64 / RPI; ++i) {
+      const int row = i * RPI + rr;
+      const int qi = wq0 + row;
+      if (qi < lq) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ost + row * Geo::OROW + cc * 16);
+        *reinterpret_cast<u32x4_t*>(out + (int64_t(qstart + qi) * hq + h) * D + cc * 8) = v;
       }
+    }
   }
 }
 
