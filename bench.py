@@ -11,12 +11,23 @@ A step is one pass of the hot path over one batch of synthetic input:
     prefill (16 sequences, shared 1024-token prefix, 512-token chunks).
 
 value = algorithmic bytes of the decode step (store + decode) / measured step time.
-roofline = the decode call (split kernel + its reduce) timed with HIP events on the
-stream it runs on: algorithmic decode bytes / average duration vs 8 TB/s.
+roofline = the decode call (stream-K kernel + its fixup kernel) timed with HIP events on
+the stream it runs on: algorithmic decode bytes / average duration vs 8 TB/s.
+traffic = HBM bytes per decode call measured by rocprofv3 counters (FETCH_SIZE and
+WRITE_SIZE, calibrated on a plain copy of known size), read from
+profiles/decode_c2_counters.json when it was taken on the current decode sources.
 cpu_baseline = the float64 CPU oracle (store_ref + decode_ref) on the same C2 batch.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-prefill]
 Prints ONE JSON line on stdout; progress goes to stderr.
+
+Counter collection (two rocprofv3 passes, then a summary written to profiles/):
+  rocprofv3 --pmc FETCH_SIZE -d DIR_F -o pass --output-format csv -- python bench.py --counter-pass
+  rocprofv3 --pmc WRITE_SIZE -d DIR_W -o pass --output-format csv -- python bench.py --counter-pass
+  python bench.py --summarize-counters DIR_F/pass_counter_collection.csv \
+                                       DIR_W/pass_counter_collection.csv
+--counter-pass runs a plain elementwise copy (torch.neg over COPY_BYTES of bf16: reads
+and writes COPY_BYTES) three times, then the decode leg only.
 """
 
 from __future__ import annotations
@@ -34,6 +45,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
+COPY_BYTES = 1 << 30            # calibration copy: 1 GiB read + 1 GiB written per launch
+DECODE_KERNELS = ("decode_streamk_kernel", "decode_fixup_kernel")
+DECODE_SOURCES = ["decode.hip", "common.hpp", "launch.hpp"]
 
 
 def log(*a):
@@ -214,6 +228,69 @@ def traffic_from_counters(kernel_sha):
     return c.get("hbm_bytes_per_decode_call")
 
 
+def counter_pass(dev, steps, warmup):
+    """Workload of a rocprofv3 --pmc pass: a copy of known size, then the decode leg."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    d = bench_decode(dev, steps, warmup)
+    print(json.dumps({"counter_pass": True, "copy_bytes": COPY_BYTES, "copy_launches": 3,
+                      "decode_calls": steps + warmup,
+                      "algorithmic_bytes_per_decode_call": int(d["dec_bytes"])}), flush=True)
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """Turn the two rocprofv3 counter CSVs of --counter-pass into profiles/ summaries."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = {}
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                e = rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])
+                e[1] += float(r["Counter_Value"])
+        return list(rows.values())
+
+    def split(rows, counter):
+        copy = [v for n, v in rows if "neg_kernel" in n]
+        calls = [v for n, v in rows if DECODE_KERNELS[0] in n]
+        dec = [v for n, v in rows if any(k in n for k in DECODE_KERNELS)]
+        if not copy or not calls:
+            raise SystemExit(f"{counter}: no copy or decode dispatches found")
+        return copy, len(calls), sum(dec)
+
+    out = {"source_sha": kernel_source_sha(DECODE_SOURCES), "copy_bytes": COPY_BYTES}
+    total = 0.0
+    for path, counter, key in ((fetch_csv, "FETCH_SIZE", "fetch"), (write_csv, "WRITE_SIZE", "write")):
+        copy, ncalls, dec_kib = split(per_dispatch(path, counter), counter)
+        copy_kib = sum(copy) / len(copy)
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        per_call = dec_kib / ncalls * 1024.0 * factor
+        total += per_call
+        out[key] = {"copy_kib_per_launch": round(copy_kib, 1), "factor": round(factor, 5),
+                    "decode_calls": ncalls, "kib_per_call_raw": round(dec_kib / ncalls, 1),
+                    "bytes_per_call": int(per_call)}
+    out["hbm_bytes_per_decode_call"] = int(total)
+    out["commands"] = [
+        "rocprofv3 --pmc FETCH_SIZE -d DIR_F -o pass --output-format csv -- "
+        "python bench.py --counter-pass --steps 10 --warmup 2",
+        "rocprofv3 --pmc WRITE_SIZE -d DIR_W -o pass --output-format csv -- "
+        "python bench.py --counter-pass --steps 10 --warmup 2",
+        "python bench.py --summarize-counters DIR_F/pass_counter_collection.csv "
+        "DIR_W/pass_counter_collection.csv"]
+    os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,7 +298,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill legs")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="copy calibration + decode leg only (run under rocprofv3 --pmc)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/decode_c2_counters.json from two --pmc passes")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the data plane shards by KV head; see the design notes)", file=sys.stderr)
@@ -237,6 +321,9 @@ def main():
         f"{props.multi_processor_count} CUs")
 
     torch.cuda.synchronize()
+    if args.counter_pass:
+        counter_pass(dev, args.steps, args.warmup)
+        return
     d = bench_decode(dev, args.steps, args.warmup)
     prefill = []
     if not args.no_prefill:
@@ -247,7 +334,7 @@ def main():
     step_bytes = d["dec_bytes"] + d["st_bytes"]
     value = step_bytes / d["ms_step"] / 1e6
     achieved = d["dec_bytes"] / d["dec_ms"] / 1e6
-    sha = kernel_source_sha(["decode.hip", "common.hpp", "launch.hpp"])
+    sha = kernel_source_sha(DECODE_SOURCES)
     case = d["case"]
     line = {
         "metric": "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% MFMA peak)",
