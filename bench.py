@@ -9,6 +9,8 @@ A step is one pass of the hot path over one batch of synthetic input:
   * prefill legs (reported beside it): 8 x 2048-token causal varlen prefill (store all
     16384 tokens, then attend through the block tables) and the prefix-cached chunked
     prefill (16 sequences, shared 1024-token prefix, 512-token chunks).
+  * long-context legs (reported beside it): decode layer by layer over all 36 layers'
+    pools for 4 x 40960 (C5a) and 256 log-uniform lengths in [128, 32768] (C5b).
 
 value = algorithmic bytes of the decode step (store + decode) / measured step time.
 roofline = the decode call (stream-K kernel + its fixup kernel) timed with HIP events on
@@ -18,7 +20,7 @@ WRITE_SIZE, calibrated on a plain copy of known size), read from
 profiles/decode_c2_counters.json when it was taken on the current decode sources.
 cpu_baseline = the float64 CPU oracle (store_ref + decode_ref) on the same C2 batch.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-prefill]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-prefill] [--no-c5]
 Prints ONE JSON line on stdout; progress goes to stderr.
 
 Counter collection (two rocprofv3 passes, then a summary written to profiles/):
@@ -175,6 +177,79 @@ def bench_prefill(dev, which, steps, warmup):
             "store_gbs": round(st_bytes / store_ms / 1e6, 1)}
 
 
+def bench_c5(dev, kind, reps, warmup):
+    """C5a / C5b: layer-by-layer decode over all 36 layers' pools (no store: the pools
+    are pre-filled).  Every layer has its own pools, so no layer finds another's K/V in
+    cache.  If the 36 layers do not fit in free device memory minus an 8 GB margin, the
+    next seed is tried (and reported)."""
+    import torch
+    import paged_kv_cache_258_amd as nkv
+    from paged_kv_cache_258_amd import accounting as acc
+    from paged_kv_cache_258_amd import workloads as wl
+
+    sh = wl.QWEN3_8B
+    base_k = 5 if kind == "a" else 6
+    torch.cuda.empty_cache()
+    free = torch.cuda.mem_get_info(dev)[0]
+    for seed_k in range(base_k, base_k + 5):
+        lens, _ = wl.c5_lengths(kind, wl.SEED_BASE + seed_k)
+        nb = sum(wl.blocks_needed(l, sh.block_size) for l in lens)
+        need = 2 * nb * sh.block_size * sh.num_kv_heads * sh.head_dim * sh.elem_bytes * wl.NUM_LAYERS
+        if need + 8e9 <= free:
+            break
+        log(f"[decode C5{kind}] seed {wl.SEED_BASE + seed_k} needs {need/1e9:.1f} GB of "
+            f"{free/1e9:.1f} GB free: next seed")
+    else:
+        return {"workload": f"C5{kind}", "skipped": f"does not fit: {free/1e9:.1f} GB free"}
+    t = time.perf_counter()
+    try:
+        mld = wl.c5_decode(kind, dev, seed_k=seed_k)
+        torch.cuda.synchronize()
+    except torch.OutOfMemoryError as e:
+        torch.cuda.empty_cache()
+        return {"workload": f"C5{kind}", "skipped": f"out of device memory: {e}"[:200]}
+    gen_s = time.perf_counter() - t
+    lens = mld.context_lens
+    lens_d = i32(lens, dev)
+    tables = [i32(layer[3], dev) for layer in mld.layers]
+    nseq = len(lens)
+    need = nkv.nkv_paged_attn_decode_workspace_size(nseq, sh.num_q_heads, sh.num_kv_heads,
+                                                    sh.head_dim, mld.layers[0][3].shape[1],
+                                                    sh.block_size)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(layer[0]) for layer in mld.layers]
+
+    def run_all():
+        for i, (q, kc, vc, _) in enumerate(mld.layers):
+            nkv.nkv_paged_attn_decode(q, kc, vc, lens_d, tables[i], sh.scale, out=outs[i],
+                                      workspace=ws)
+
+    for _ in range(warmup):
+        run_all()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run_all()
+    e1.record()
+    torch.cuda.synchronize()
+    per_layer_ms = e0.elapsed_time(e1) / reps / wl.NUM_LAYERS
+    nbytes = acc.decode_bytes(lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                              sh.elem_bytes)
+    gbs = nbytes / per_layer_ms / 1e6
+    log(f"[decode C5{kind}] {wl.NUM_LAYERS} layers, per layer {per_layer_ms*1e3:.1f} us -> "
+        f"{gbs:.0f} GB/s (sum ctx {int(lens.sum())}, generated in {gen_s:.1f}s)")
+    res = {"workload": f"C5{kind}", "seed": wl.SEED_BASE + seed_k, "num_seqs": nseq,
+           "sum_context_tokens": int(lens.sum()), "layers": wl.NUM_LAYERS, "reps": reps,
+           "per_layer_us": round(per_layer_ms * 1e3, 2),
+           "all_layers_ms": round(per_layer_ms * wl.NUM_LAYERS, 3),
+           "decode_bytes_per_layer": int(nbytes), "gbs": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del mld, tables, outs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(case, budget_s=10.0):
     """The float64 oracle (store_ref + decode_ref) on the full C2 batch, on host cores."""
     import numpy as np
@@ -298,6 +373,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill legs")
+    ap.add_argument("--no-c5", action="store_true", help="skip the 36-layer C5a/C5b decode legs")
     ap.add_argument("--counter-pass", action="store_true",
                     help="copy calibration + decode leg only (run under rocprofv3 --pmc)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -329,6 +405,10 @@ def main():
     if not args.no_prefill:
         prefill.append(bench_prefill(dev, "C3", max(5, args.steps // 2), 2))
         prefill.append(bench_prefill(dev, "C4", max(5, args.steps // 2), 2))
+    long_decode = []
+    if not args.no_c5:
+        for kind in ("a", "b"):
+            long_decode.append(bench_c5(dev, kind, 5, 1))
     cpu = None if args.no_cpu else cpu_baseline(d["case"])
 
     step_bytes = d["dec_bytes"] + d["st_bytes"]
@@ -375,6 +455,7 @@ def main():
         "store": {"avg_launch_us": round(d["store_ms"] * 1e3, 2),
                   "gbs": round(d["st_bytes"] / d["store_ms"] / 1e6, 1)},
         "prefill": prefill,
+        "long_decode": long_decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

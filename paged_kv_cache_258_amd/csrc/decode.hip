@@ -470,22 +470,46 @@ decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_
   auto owner = [&](int64_t t) { return int(((t + 1) * W - 1) / R); };
   const int w0 = owner(s), w1 = owner(e - 1);
   if (w0 == w1) return;                      // finished in place
-  float M = -INFINITY;
-  for (int w = w0; w <= w1; ++w) {
+  // Lane i handles pieces i, i+64, ...: their (m, l) loads are independent, and the
+  // partial rows are then summed in piece order with many loads in flight.
+  const int lane = threadIdx.x;
+  const int np = w1 - w0 + 1;
+  auto slot_of = [&](int w) {
     const int k = (int64_t(w) * R / W >= s) ? 0 : 1;
-    M = fmaxf(M, ws_ml[((int64_t(w) * 2 + k) * G + col) * 2]);
-  }
+    return (w * 2 + k) * G + col;
+  };
+  float M = -INFINITY;
+  for (int i = lane; i < np; i += 64) M = fmaxf(M, ws_ml[int64_t(slot_of(w0 + i)) * 2]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float den = 0.f, num[DPT];
 #pragma unroll
   for (int j = 0; j < DPT; ++j) num[j] = 0.f;
-  for (int w = w0; w <= w1; ++w) {
-    const int k = (int64_t(w) * R / W >= s) ? 0 : 1;
-    const int64_t slot = (int64_t(w) * 2 + k) * G + col;
-    const float wt = fast_exp2(ws_ml[slot * 2] - M);
-    den = fmaf(wt, ws_ml[slot * 2 + 1], den);
+  for (int c0 = 0; c0 < np; c0 += 64) {
+    const int i = c0 + lane;
+    int my_slot = 0;
+    float wt = 0.f;
+    if (i < np) {
+      my_slot = slot_of(w0 + i);
+      wt = fast_exp2(ws_ml[int64_t(my_slot) * 2] - M);
+      den = fmaf(wt, ws_ml[int64_t(my_slot) * 2 + 1], den);
+    }
+    const int n = np - c0 < 64 ? np - c0 : 64;
+    auto add = [&](int jp) {
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), jp));
+      const int64_t sj = __builtin_amdgcn_readlane(my_slot, jp);
 #pragma unroll
-    for (int j = 0; j < DPT; ++j) num[j] = fmaf(wt, ws_part[slot * D + threadIdx.x + 64 * j], num[j]);
+      for (int j = 0; j < DPT; ++j) num[j] = fmaf(wj, ws_part[sj * D + lane + 64 * j], num[j]);
+    };
+    int jp = 0;
+    for (; jp + 8 <= n; jp += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) add(jp + u);
+    }
+    for (; jp < n; ++jp) add(jp);
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
   const float inv = 1.0f / den;
   const int64_t row = int64_t(b) * num_kv_heads * G + h;
 #pragma unroll

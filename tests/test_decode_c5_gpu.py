@@ -1,0 +1,76 @@
+"""Decode parity at full size on the two 36-layer configurations:
+
+* C5a -- 4 sequences at context 40960 (the model's maximum position), Qwen3-8B heads,
+  block_size 256, bf16;
+* C5b -- 256 sequences, lengths log-uniform in [128, 32768].
+
+Each layer has its own pools, block tables and values.  Layers 0, 17 and 35 are
+materialised at their full size and decoded exactly as bench.py launches them (the
+whole batch, default plan).  The oracle checks every sequence of C5a and a seeded
+sample of C5b (the longest, the shortest and six drawn at random), reading a compact
+host copy of just the sampled sequences' blocks with the block table renumbered to
+match (a gather of whole blocks: no arithmetic).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from paged_kv_cache_258_amd import nkv_paged_attn_decode
+from paged_kv_cache_258_amd import workloads as wl
+
+from _gpu_helpers import assert_close, dev_i32, host_bits, log, require_gpu, to_f64
+
+pytestmark = pytest.mark.gpu
+
+LAYERS = [0, 17, 35]
+
+
+def compact(kc, vc, table, lens, seqs, bs):
+    """Host copies of the blocks the sampled sequences use, with a renumbered table."""
+    used = []
+    for b in seqs:
+        used.extend(int(x) for x in table[b, :wl.blocks_needed(lens[b], bs)])
+    uniq = sorted(set(used))
+    remap = {old: new for new, old in enumerate(uniq)}
+    idx = torch.as_tensor(uniq, dtype=torch.int64, device=kc.device)
+    kh = host_bits(kc.index_select(0, idx))
+    vh = host_bits(vc.index_select(0, idx))
+    sub = np.full((len(seqs), table.shape[1]), -1, dtype=np.int32)
+    for i, b in enumerate(seqs):
+        n = wl.blocks_needed(lens[b], bs)
+        sub[i, :n] = [remap[int(x)] for x in table[b, :n]]
+    return kh, vh, sub
+
+
+def sample_seqs(kind, lens):
+    if kind == "a":
+        return list(range(len(lens)))
+    rng = np.random.default_rng(2580)
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    while len(pick) < 8:
+        pick.add(int(rng.integers(len(lens))))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("kind", ["a", "b"])
+def test_decode_c5_full_size_sampled(kind):
+    dev = require_gpu()
+    mld = wl.c5_decode(kind, dev, layers=LAYERS)
+    sh = mld.shape
+    lens = mld.context_lens
+    seqs = sample_seqs(kind, lens)
+    log(f"[decode C5{kind}] B={len(lens)} sum_ctx={int(lens.sum())} layers={LAYERS} "
+        f"checked seqs={seqs} (lens {[int(lens[b]) for b in seqs]})")
+    lens_d = dev_i32(lens, dev)
+    for layer, (q, kc, vc, table) in zip(LAYERS, mld.layers):
+        out = nkv_paged_attn_decode(q, kc, vc, lens_d, dev_i32(table, dev), sh.scale)
+        torch.cuda.synchronize()
+        got = to_f64(out)[seqs]
+        kh, vh, sub = compact(kc, vc, table, lens, seqs, sh.block_size)
+        want = ref.decode_ref(host_bits(q)[seqs], kh, vh, lens[seqs], sub, sh.scale, elem="bf16")
+        assert_close(got, want, f"C5{kind} layer {layer}")
+        del out, kh, vh
+    del mld
+    torch.cuda.empty_cache()
