@@ -33,6 +33,13 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-source flags.  prefill.hip: keep MFMA accumulators and results in VGPRs; with
+# the default heuristic the O^T accumulators live in AGPRs and every loop iteration
+# copies all of them to VGPRs and back around the (rarely taken) rescale branch.
+SOURCE_FLAGS = {
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -56,8 +63,8 @@ def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BU
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
-                     "-o", obj])
+        cmds.append([hipcc, *FLAGS, *SOURCE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
         for r in ex.map(_run, cmds):
             noise = ("packed-fp32-ops", "warning: argument unused")

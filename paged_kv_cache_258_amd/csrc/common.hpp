@@ -93,6 +93,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait for every outstanding vector memory operation, through the builtin so that the
+// compiler's own wait-count tracking learns that register loads issued before it have
+// landed (after an asm wait it would still guard their registers with another full wait).
+// Encoding (gfx9): vmcnt[3:0]=0, expcnt[6:4]=7, lgkmcnt[11:8]=15, vmcnt[15:14]=0.
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
+
 // Global -> LDS copies (global_load_lds, 16 or 4 bytes per lane; lane i writes
 // lds_base + i*size, lds_base the same for the whole wave).  They are issued through
 // inline asm so that the compiler neither tracks them nor guards every later LDS read

@@ -38,15 +38,17 @@
 namespace nkv {
 
 constexpr int kBK = 64;                 // keys per tile
+constexpr int kStages = 2;              // K/V tiles in LDS (one computed, one landing)
 constexpr float kLazy = 8.0f;           // log2 headroom before rescaling
 constexpr int kVPad = 8;                // bf16 elements of padding per Vt row in LDS
+constexpr int kNW = 8;                  // waves per workgroup (two per SIMD)
+constexpr int kMaxIds = 4;              // block ids per tile (block_size >= 16)
 
 template <int D, int G>
 struct PfGeom {
-  static constexpr int NW = G > 4 ? G : 4;      // waves per workgroup
-  static constexpr int NT = NW * kWave;
-  static constexpr int QSUB = NW / G;           // 64-query sub-tiles per workgroup
-  static constexpr int BQ = 64 * QSUB;          // queries per workgroup
+  static constexpr int NT = kNW * kWave;
+  static constexpr int QSUB = kNW / G;          // 32-query sub-tiles per workgroup
+  static constexpr int BQ = 32 * QSUB;          // queries per workgroup
   static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DT = D / 32;             // 32-dim tiles of O^T
   static constexpr int CPR = D / 8;             // 16-byte chunks per K row
@@ -54,12 +56,13 @@ struct PfGeom {
   static constexpr int VROW = kBK + kVPad;      // Vt row stride (elements)
   static constexpr int VT_BYTES = D * VROW * 2;
   static constexpr int STAGE = K_BYTES + VT_BYTES;
-  static constexpr int K_DMA = K_BYTES / 1024 / NW;   // K copy instructions per wave per tile
-  static constexpr int V_ITEMS = (kBK / 4) * CPR;     // (key quad, chunk) items per tile
+  static constexpr int K_DMA = K_BYTES / 1024 / kNW;  // K copy instructions per wave per tile
+  static constexpr int V_ITEMS = (kBK / 2) * CPR;     // (key pair, chunk) items per tile
   static constexpr int OROW = D * 2 + 8;              // output staging row stride (bytes)
-  static_assert(K_BYTES % (1024 * NW) == 0, "K tile must split evenly over the waves");
+  static_assert(G >= 1 && G <= kNW && kNW % G == 0, "GQA group must divide the waves");
+  static_assert(K_DMA >= 1 && K_BYTES % (1024 * kNW) == 0, "K tile must split over the waves");
   static_assert(V_ITEMS <= NT, "one V item per thread");
-  static constexpr int SMEM = 2 * STAGE > NW * 64 * OROW ? 2 * STAGE : NW * 64 * OROW;
+  static constexpr int SMEM = kStages * STAGE > kNW * 32 * OROW ? kStages * STAGE : kNW * 32 * OROW;
 };
 
 // Position of key quad kq (keys 4kq..4kq+3) of a tile inside the transposed V rows:
@@ -70,7 +73,7 @@ __device__ __forceinline__ int vt_quad_pos(int kq) {
 }
 
 template <int D, int G>
-__global__ void __launch_bounds__((G > 4 ? G : 4) * 64)
+__global__ void __launch_bounds__(kNW * 64)
 prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
@@ -78,8 +81,9 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     int32_t num_kv_heads, int32_t log2_bs, float scale_log2e,
                     uint16_t* __restrict__ out) {
   using Geo = PfGeom<D, G>;
-  constexpr int NT = Geo::NT, KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, VROW = Geo::VROW;
+  constexpr int KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, VROW = Geo::VROW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Geo::SMEM];
+  __shared__ int32_t s_ids[3][kMaxIds];               // block ids of tiles t, t+1, t+2
 
   const int pair = blockIdx.x;
   const int b = pair / num_kv_heads;
@@ -99,31 +103,42 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int hq = G * num_kv_heads;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int wq0 = q0 + (wave / G) * 64;               // this wave's first query
+  const int wq0 = q0 + (wave / G) * 32;               // this wave's first query
   const int kend = diag + min(q0 + Geo::BQ, lq);      // keys the workgroup needs
   const int ntiles = (kend + kBK - 1) / kBK;
-  const int wkend = wq0 < lq ? diag + min(wq0 + 64, lq) : 0;   // keys this wave needs
+  const int wkend = wq0 < lq ? diag + min(wq0 + 32, lq) : 0;   // keys this wave needs
   const int32_t* __restrict__ trow = block_table + int64_t(b) * max_blocks;
   const int bs_mask = (1 << log2_bs) - 1;
+  const int last_blk = (lk > 0 ? lk - 1 : 0) >> log2_bs;
+  const int ids_per_tile = log2_bs >= 6 ? 1 : (kBK >> log2_bs);
   const int64_t row_elems = int64_t(num_kv_heads) * D;
   const uint16_t* kbase = k_cache + int64_t(g) * D;
   const uint16_t* vbase = v_cache + int64_t(g) * D;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): two 32-query blocks, 8 dims per lane ----
-  bf16x8_t qf[2][KS];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = wq0 + qb * 32 + l32;
+  // ---- Q fragments (B operand of S^T = K Q^T): 32 queries, 8 dims per lane and k-step ----
+  bf16x8_t qf[KS];
+  {
+    const int qi = wq0 + l32;
     const bool ok = qi < lq;
     const uint16_t* qp = q + int64_t(qstart + (ok ? qi : 0)) * q_row + int64_t(h) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
-      qf[qb][ks] = __builtin_bit_cast(bf16x8_t, v);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
-  // ---- tile copies: K rows by DMA (this wave's share), V (one item per thread) to regs ----
+  // ---- copies: block ids two tiles ahead (LDS), K rows by DMA, V through registers ----
+  auto issue_ids = [&](int t) {                       // wave 0: ids of tile t -> s_ids[t % 3]
+    if (wave == 0 && lane < ids_per_tile) {
+      const int blk = min(((t * kBK) >> log2_bs) + lane, last_blk);
+      load_lds4(trow + blk, &s_ids[t % 3][0]);
+    }
+  };
+  auto row_off = [&](int t, int key) -> int64_t {     // element offset of (key, head g)
+    const int64_t phys = s_ids[t % 3][((key - t * kBK) >> log2_bs) & (kMaxIds - 1)];
+    return ((phys << log2_bs) + (key & bs_mask)) * row_elems;
+  };
   int k_row[Geo::K_DMA], k_elem[Geo::K_DMA];
 #pragma unroll
   for (int j = 0; j < Geo::K_DMA; ++j) {
@@ -131,138 +146,119 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     k_row[j] = s / CPR;
     k_elem[j] = ((s % CPR) ^ (k_row[j] & (CPR - 1))) * 8;
   }
-  const bool v_item = tid < Geo::V_ITEMS;
-  const int v_kq = tid % 16, v_c = tid / 16;
-  auto row_off = [&](int key) -> int64_t {          // element offset of (key, head g)
-    const int64_t phys = trow[key >> log2_bs];
-    return ((phys << log2_bs) + (key & bs_mask)) * row_elems;
-  };
   auto issue_k = [&](int t) {
-    uint8_t* sk = smem + (t & 1) * Geo::STAGE;
+    uint8_t* sk = smem + (t % kStages) * Geo::STAGE;
 #pragma unroll
     for (int j = 0; j < Geo::K_DMA; ++j) {
       const int key = min(t * kBK + k_row[j], lk - 1);
-      load_lds16(kbase + row_off(key) + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
+      load_lds16(kbase + row_off(t, key) + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
     }
   };
-  u32x4_t vreg[4];
+  const bool v_item = tid < Geo::V_ITEMS;
+  const int v_kp = tid % 32, v_c = tid / 32;          // key pair, 16-byte chunk
+  u32x4_t vreg[2];
   auto load_v = [&](int t) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = t * kBK + 4 * v_kq + j;
-      vreg[j] = (v_item && key < lk)
-                    ? *reinterpret_cast<const u32x4_t*>(vbase + row_off(key) + v_c * 8)
+    for (int j = 0; j < 2; ++j) {
+      const int key = t * kBK + 2 * v_kp + j;
+      vreg[j] = (v_item && key < lk)                  // rows past the keys are zero, not NaN
+                    ? *reinterpret_cast<const u32x4_t*>(vbase + row_off(t, key) + v_c * 8)
                     : u32x4_t{0, 0, 0, 0};
     }
   };
-  auto commit_v = [&](int t) {
+  auto commit_v = [&](int t) {                        // keys 2kp, 2kp+1 of 8 dims -> Vt
     if (!v_item) return;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(smem + (t & 1) * Geo::STAGE + Geo::K_BYTES);
-    const int pos = 4 * vt_quad_pos(v_kq);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(smem + (t % kStages) * Geo::STAGE + Geo::K_BYTES);
+    const int pos = 4 * vt_quad_pos(v_kp >> 1) + 2 * (v_kp & 1);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {       // dims 2w, 2w+1 of this chunk: 4 keys each
-      const uint32_t a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
-      const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-      const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-      *reinterpret_cast<u32x2_t*>(&vt[(v_c * 8 + 2 * w) * VROW + pos]) = lo;
-      *reinterpret_cast<u32x2_t*>(&vt[(v_c * 8 + 2 * w + 1) * VROW + pos]) = hi;
+    for (int w = 0; w < 4; ++w) {                     // dims 2w, 2w+1 of the chunk
+      const uint32_t lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
+      const uint32_t hi = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
+      *reinterpret_cast<uint32_t*>(&vt[(v_c * 8 + 2 * w) * VROW + pos]) = lo;
+      *reinterpret_cast<uint32_t*>(&vt[(v_c * 8 + 2 * w + 1) * VROW + pos]) = hi;
     }
   };
 
-  f32x16_t o[2][DT];
+  f32x16_t o[DT];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][dt][r] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m = -INFINITY;
+  float lsum = 0.f;
   const uint32_t ones = 0x3f803f80u;   // bf16 pair (1, 1)
 
-  // S^T for one 32-key half of the tile in stage `sk`
-  auto qk = [&](const uint8_t* sk, int kb, f32x16_t (&s)[2]) {
+  // One 32-key half `kb` of the tile in stage `st`: S^T = K Q^T, softmax, O^T += V^T P^T.
+  auto half = [&](const uint8_t* st, int kb, int k0h) {
+    f32x16_t s;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
     const int t = kb * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-          sk + (t * CPR + ((2 * ks + hh) ^ (t & (CPR - 1)))) * 16);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb], 0, 0, 0);
+          st + (t * CPR + ((2 * ks + hh) ^ (t & (CPR - 1)))) * 16);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
     }
-  };
-  // softmax of one half: mask (if needed), lazy max, P as bf16 in P.V key order.
-  // Masked halves are scaled before the mask is applied (cs = 1 afterwards) so that a
-  // zero softmax_scale cannot turn -inf into NaN; unmasked halves fold the scale into
-  // the exponent's FMA.
-  auto softmax = [&](f32x16_t (&s)[2], int k0h, bf16x8_t (&pf)[2][2]) {
+    // Masked halves are scaled before the mask is applied (cs = 1 afterwards) so that
+    // a zero softmax_scale cannot turn -inf into NaN; unmasked halves fold the scale
+    // into the exponent's FMA.
     const bool masked = (k0h + 31 > diag + wq0) || (k0h + 32 > lk);
     const float cs = masked ? 1.0f : scale_log2e;
-    float mx[2];
+    if (masked) {
+      const int qi = wq0 + l32;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      if (masked) {
-        const int qi = wq0 + qb * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0h + 8 * (r >> 2) + 4 * hh + (r & 3);
-          s[qb][r] = (key < lk && key <= diag + qi) ? s[qb][r] * scale_log2e : -INFINITY;
-        }
-      }
-      float x = s[qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[qb][r]);
-      mx[qb] = xor32_max(x) * cs;
-    }
-    if (__any(mx[0] > m[0] + kLazy || mx[1] > m[1] + kLazy)) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float mn = fmaxf(m[qb], mx[qb]);
-        const float alpha = fast_exp2(m[qb] - mn);
-        lsum[qb] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha;
-        m[qb] = mn;
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0h + 8 * (r >> 2) + 4 * hh + (r & 3);
+        s[r] = (key < lk && key <= diag + qi) ? s[r] * scale_log2e : -INFINITY;
       }
     }
+    float x = s[0];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int r = 1; r < 16; ++r) x = fmaxf(x, s[r]);
+    const float mx = xor32_max(x) * cs;
+    if (__any(mx > m + kLazy)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      lsum *= alpha;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4_t w;
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m = mn;
+    }
+    bf16x8_t pf[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = fast_exp2(fmaf(s[qb][8 * kk + 2 * i], cs, -m[qb]));
-          const float p1 = fast_exp2(fmaf(s[qb][8 * kk + 2 * i + 1], cs, -m[qb]));
-          w[i] = pack_bf16x2(p0, p1);
-          lsum[qb] = dot2_bf16(w[i], ones, lsum[qb]);
-        }
-        pf[qb][kk] = __builtin_bit_cast(bf16x8_t, w);
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4_t w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = fast_exp2(fmaf(s[8 * kk + 2 * i], cs, -m));
+        const float p1 = fast_exp2(fmaf(s[8 * kk + 2 * i + 1], cs, -m));
+        w[i] = pack_bf16x2(p0, p1);
+        lsum = dot2_bf16(w[i], ones, lsum);
       }
-  };
-  auto pv = [&](const uint8_t* sv, int kb, const bf16x8_t (&pf)[2][2]) {
+      pf[kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    const uint8_t* sv = st + Geo::K_BYTES;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
             sv + ((dt * 32 + l32) * VROW + kb * 32 + kk * 16 + 8 * hh) * 2);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kk], o[qb][dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[dt], 0, 0, 0);
       }
   };
 
-  // ---- prologue: tile 0 into stage 0 ----
+  // ---- prologue: ids of tiles 0..2, tile 0 into stage 0 ----
+  issue_ids(0);
+  if (ntiles > 1) issue_ids(1);
+  wait_vmem_all();
+  __syncthreads();
   issue_k(0);
   load_v(0);
+  if (ntiles > 2) issue_ids(2);
+  wait_vmem_all();
   commit_v(0);
-  wait_vmcnt<0>();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -270,50 +266,37 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     if (more) {                                   // next tile's copies fly during this one
       issue_k(t + 1);
       load_v(t + 1);
+      if (t + 3 < ntiles) issue_ids(t + 3);
     }
     const int k0 = t * kBK;
-    if (k0 < wkend) {
-      const uint8_t* sk = smem + (t & 1) * Geo::STAGE;
-      const uint8_t* sv = sk + Geo::K_BYTES;
-      f32x16_t s0[2], s1[2];
-      bf16x8_t p0[2][2], p1[2][2];
-      qk(sk, 0, s0);
-      softmax(s0, k0, p0);
-      pv(sv, 0, p0);
-      if (k0 + 32 < wkend) {
-        qk(sk, 1, s1);
-        softmax(s1, k0 + 32, p1);
-        pv(sv, 1, p1);
-      }
-    }
+    const uint8_t* st = smem + (t % kStages) * Geo::STAGE;
+    if (k0 < wkend) half(st, 0, k0);
+    if (k0 + 32 < wkend) half(st, 1, k0 + 32);
+    wait_vmem_all();
     if (more) commit_v(t + 1);
-    wait_vmcnt<0>();
     __syncthreads();
   }
 
   // ---- epilogue: O^T / l -> bf16 rows staged in LDS, then contiguous row writes ----
-  uint8_t* ost = smem + wave * 64 * Geo::OROW;
+  uint8_t* ost = smem + wave * 32 * Geo::OROW;
   if (wq0 < lq) {
+    const float inv = 1.0f / xor32_sum(lsum);     // the two lane halves hold different keys
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float inv = 1.0f / xor32_sum(lsum[qb]);   // the two lane halves hold different keys
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = dt * 32 + 8 * r4 + 4 * hh;
-          const u32x2_t w = {pack_bf16x2(o[qb][dt][4 * r4 + 0] * inv, o[qb][dt][4 * r4 + 1] * inv),
-                             pack_bf16x2(o[qb][dt][4 * r4 + 2] * inv, o[qb][dt][4 * r4 + 3] * inv)};
-          *reinterpret_cast<u32x2_t*>(ost + (qb * 32 + l32) * Geo::OROW + d0 * 2) = w;
-        }
-    }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = dt * 32 + 8 * r4 + 4 * hh;
+        const u32x2_t w = {pack_bf16x2(o[dt][4 * r4 + 0] * inv, o[dt][4 * r4 + 1] * inv),
+                           pack_bf16x2(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv)};
+        *reinterpret_cast<u32x2_t*>(ost + l32 * Geo::OROW + d0 * 2) = w;
+      }
   }
   __syncthreads();
   if (wq0 < lq) {
     constexpr int RPI = 64 / CPR;                 // rows per 64-lane pass
     const int rr = lane / CPR, cc = lane % CPR;
 #pragma unroll
-    for (int i = 0; i < 64 / RPI; ++i) {
+    for (int i = 0; i < 32 / RPI; ++i) {
       const int row = i * RPI + rr;
       const int qi = wq0 + row;
       if (qi < lq) {
