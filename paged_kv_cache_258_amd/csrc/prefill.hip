@@ -188,21 +188,42 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   float lsum = 0.f;
   const uint32_t ones = 0x3f803f80u;   // bf16 pair (1, 1)
 
-  // One 32-key half `kb` of the tile in stage `st`: S^T = K Q^T, softmax, O^T += V^T P^T.
-  auto half = [&](const uint8_t* st, int kb, int k0h) {
-    f32x16_t s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  // Fragments of the 32-key half `kb` of the tile in stage `st`: K rows (A operand of
+  // S^T = K Q^T) and V^T rows (A operand of O^T += V^T P^T).  They are read ahead of
+  // their MFMAs so that LDS latency overlaps the softmax.
+  auto read_k = [&](const uint8_t* st, int kb, bf16x8_t (&kf)[KS]) {
     const int t = kb * 32 + l32;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-          st + (t * CPR + ((2 * ks + hh) ^ (t & (CPR - 1)))) * 16);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-    }
-    // Masked halves are scaled before the mask is applied (cs = 1 afterwards) so that
-    // a zero softmax_scale cannot turn -inf into NaN; unmasked halves fold the scale
-    // into the exponent's FMA.
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8_t*>(st + (t * CPR + ((2 * ks + hh) ^ (t & (CPR - 1)))) * 16);
+  };
+  auto read_v = [&](const uint8_t* st, int kb, bf16x8_t (&vf)[2][DT]) {
+    const uint8_t* sv = st + Geo::K_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        vf[kk][dt] = *reinterpret_cast<const bf16x8_t*>(
+            sv + ((dt * 32 + l32) * VROW + kb * 32 + kk * 16 + 8 * hh) * 2);
+  };
+  auto qk = [&](const bf16x8_t (&kf)[KS], f32x16_t& s) {
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16_t{}, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+  };
+  auto pv = [&](const bf16x8_t (&vf)[2][DT], const bf16x8_t (&pf)[2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][dt], pf[kk], o[dt], 0, 0, 0);
+  };
+  // Softmax of one half: mask (if needed), lazy max, P as bf16 in P.V key order.
+  // Masked halves are scaled before the mask is applied (cs = 1 afterwards) so that a
+  // zero softmax_scale cannot turn -inf into NaN; unmasked halves fold the scale into
+  // the exponent's FMA.
+  auto softmax = [&](f32x16_t& s, int k0h, bf16x8_t (&pf)[2]) {
     const bool masked = (k0h + 31 > diag + wq0) || (k0h + 32 > lk);
     const float cs = masked ? 1.0f : scale_log2e;
     if (masked) {
@@ -225,7 +246,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
       m = mn;
     }
-    bf16x8_t pf[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4_t w;
@@ -238,15 +258,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       }
       pf[kk] = __builtin_bit_cast(bf16x8_t, w);
     }
-    const uint8_t* sv = st + Geo::K_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            sv + ((dt * 32 + l32) * VROW + kb * 32 + kk * 16 + 8 * hh) * 2);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[dt], 0, 0, 0);
-      }
   };
 
   // ---- prologue: ids of tiles 0..2, tile 0 into stage 0 ----
@@ -270,8 +281,25 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     }
     const int k0 = t * kBK;
     const uint8_t* st = smem + (t % kStages) * Geo::STAGE;
-    if (k0 < wkend) half(st, 0, k0);
-    if (k0 + 32 < wkend) half(st, 1, k0 + 32);
+    if (k0 < wkend) {
+      // half 0, with half 0's V^T and half 1's K fragments read before its softmax
+      bf16x8_t kf0[KS], kf1[KS], vf[2][DT], pf[2];
+      f32x16_t s;
+      read_k(st, 0, kf0);
+      qk(kf0, s);
+      read_v(st, 0, vf);
+      read_k(st, 1, kf1);                         // always in bounds; unused if no half 1
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(s, k0, pf);
+      pv(vf, pf);
+      if (k0 + 32 < wkend) {
+        qk(kf1, s);
+        read_v(st, 1, vf);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax(s, k0 + 32, pf);
+        pv(vf, pf);
+      }
+    }
     wait_vmem_all();
     if (more) commit_v(t + 1);
     __syncthreads();
