@@ -37,18 +37,31 @@
 
 namespace nkv {
 
-constexpr int kBK = 64;                 // keys per tile
+#ifndef NKV_PREFILL_QB
+#define NKV_PREFILL_QB 1
+#endif
+#ifndef NKV_PREFILL_BK
+#define NKV_PREFILL_BK 128
+#endif
+
+constexpr int kBK = NKV_PREFILL_BK;     // keys per tile (a multiple of 32)
 constexpr int kStages = 2;              // K/V tiles in LDS (one computed, one landing)
 constexpr float kLazy = 8.0f;           // log2 headroom before rescaling
 constexpr int kVPad = 8;                // bf16 elements of padding per Vt row in LDS
-constexpr int kNW = 8;                  // waves per workgroup (two per SIMD)
-constexpr int kMaxIds = 4;              // block ids per tile (block_size >= 16)
+constexpr int kMaxIds = kBK / 16;       // block ids per tile (block_size >= 16)
+constexpr int kLog2BK = kBK == 128 ? 7 : 6;
+static_assert(kBK == 64 || kBK == 128, "64- or 128-key tiles");
 
-template <int D, int G>
+// QB: 32-query blocks per wave.  QB = 1: eight waves of 32 queries (two per SIMD);
+// QB = 2: four waves of 64 queries (one per SIMD), each K/V fragment read from LDS
+// feeding two MFMAs.
+template <int D, int G, int QB>
 struct PfGeom {
-  static constexpr int NT = kNW * kWave;
-  static constexpr int QSUB = kNW / G;          // 32-query sub-tiles per workgroup
-  static constexpr int BQ = 32 * QSUB;          // queries per workgroup
+  static constexpr int NW = 8 / QB;             // waves per workgroup
+  static constexpr int NT = NW * kWave;
+  static constexpr int WQ = 32 * QB;            // queries per wave
+  static constexpr int QSUB = NW / G;           // query sub-tiles per workgroup
+  static constexpr int BQ = WQ * QSUB;          // queries per workgroup
   static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DT = D / 32;             // 32-dim tiles of O^T
   static constexpr int CPR = D / 8;             // 16-byte chunks per K row
@@ -56,13 +69,15 @@ struct PfGeom {
   static constexpr int VROW = kBK + kVPad;      // Vt row stride (elements)
   static constexpr int VT_BYTES = D * VROW * 2;
   static constexpr int STAGE = K_BYTES + VT_BYTES;
-  static constexpr int K_DMA = K_BYTES / 1024 / kNW;  // K copy instructions per wave per tile
-  static constexpr int V_ITEMS = (kBK / 2) * CPR;     // (key pair, chunk) items per tile
-  static constexpr int OROW = D * 2 + 8;              // output staging row stride (bytes)
-  static_assert(G >= 1 && G <= kNW && kNW % G == 0, "GQA group must divide the waves");
-  static_assert(K_DMA >= 1 && K_BYTES % (1024 * kNW) == 0, "K tile must split over the waves");
+  static constexpr int K_DMA = K_BYTES / 1024 / NW;   // K copy instructions per wave per tile
+  static constexpr int KPI = kBK * CPR / NT > 2 ? kBK * CPR / NT : 2;   // keys per V item
+  static_assert(KPI == 2 || KPI == 4, "V items of 2 or 4 keys");
+  static constexpr int V_ITEMS = (kBK / KPI) * CPR;   // (key group, chunk) items per tile
+  static constexpr int OROW = D * 2 + 16;             // output staging row stride (bytes)
+  static_assert(G >= 1 && G <= NW && NW % G == 0, "GQA group must divide the waves");
+  static_assert(K_DMA >= 1 && K_BYTES % (1024 * NW) == 0, "K tile must split over the waves");
   static_assert(V_ITEMS <= NT, "one V item per thread");
-  static constexpr int SMEM = kStages * STAGE > kNW * 32 * OROW ? kStages * STAGE : kNW * 32 * OROW;
+  static constexpr int SMEM = kStages * STAGE > NW * WQ * OROW ? kStages * STAGE : NW * WQ * OROW;
 };
 
 // Position of key quad kq (keys 4kq..4kq+3) of a tile inside the transposed V rows:
@@ -72,16 +87,16 @@ __device__ __forceinline__ int vt_quad_pos(int kq) {
   return (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
 }
 
-template <int D, int G>
-__global__ void __launch_bounds__(kNW * 64)
+template <int D, int G, int QB>
+__global__ void __launch_bounds__(8 / QB * 64)
 prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                     const int32_t* __restrict__ block_table, int32_t max_blocks,
                     int32_t num_kv_heads, int32_t log2_bs, float scale_log2e,
                     uint16_t* __restrict__ out) {
-  using Geo = PfGeom<D, G>;
-  constexpr int KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, VROW = Geo::VROW;
+  using Geo = PfGeom<D, G, QB>;
+  constexpr int KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, VROW = Geo::VROW, WQ = Geo::WQ;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Geo::SMEM];
   __shared__ int32_t s_ids[3][kMaxIds];               // block ids of tiles t, t+1, t+2
 
@@ -103,28 +118,29 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int hq = G * num_kv_heads;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int wq0 = q0 + (wave / G) * 32;               // this wave's first query
+  const int wq0 = q0 + (wave / G) * WQ;               // this wave's first query
   const int kend = diag + min(q0 + Geo::BQ, lq);      // keys the workgroup needs
   const int ntiles = (kend + kBK - 1) / kBK;
-  const int wkend = wq0 < lq ? diag + min(wq0 + 32, lq) : 0;   // keys this wave needs
+  const int wkend = wq0 < lq ? diag + min(wq0 + WQ, lq) : 0;   // keys this wave needs
   const int32_t* __restrict__ trow = block_table + int64_t(b) * max_blocks;
   const int bs_mask = (1 << log2_bs) - 1;
   const int last_blk = (lk > 0 ? lk - 1 : 0) >> log2_bs;
-  const int ids_per_tile = log2_bs >= 6 ? 1 : (kBK >> log2_bs);
+  const int ids_per_tile = log2_bs >= kLog2BK ? 1 : (kBK >> log2_bs);
   const int64_t row_elems = int64_t(num_kv_heads) * D;
   const uint16_t* kbase = k_cache + int64_t(g) * D;
   const uint16_t* vbase = v_cache + int64_t(g) * D;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): 32 queries, 8 dims per lane and k-step ----
-  bf16x8_t qf[KS];
-  {
-    const int qi = wq0 + l32;
+  // ---- Q fragments (B operand of S^T = K Q^T): per 32-query block, 8 dims per lane ----
+  bf16x8_t qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = wq0 + qb * 32 + l32;
     const bool ok = qi < lq;
     const uint16_t* qp = q + int64_t(qstart + (ok ? qi : 0)) * q_row + int64_t(h) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
@@ -154,43 +170,61 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       load_lds16(kbase + row_off(t, key) + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
     }
   };
+  constexpr int KPI = Geo::KPI;
   const bool v_item = tid < Geo::V_ITEMS;
-  const int v_kp = tid % 32, v_c = tid / 32;          // key pair, 16-byte chunk
-  u32x4_t vreg[2];
+  const int v_kg = tid % (kBK / KPI), v_c = tid / (kBK / KPI);   // key group, 16-byte chunk
+  u32x4_t vreg[KPI];
   auto load_v = [&](int t) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int key = t * kBK + 2 * v_kp + j;
+    for (int j = 0; j < KPI; ++j) {
+      const int key = t * kBK + KPI * v_kg + j;
       vreg[j] = (v_item && key < lk)                  // rows past the keys are zero, not NaN
                     ? *reinterpret_cast<const u32x4_t*>(vbase + row_off(t, key) + v_c * 8)
                     : u32x4_t{0, 0, 0, 0};
     }
   };
-  auto commit_v = [&](int t) {                        // keys 2kp, 2kp+1 of 8 dims -> Vt
+  auto commit_v = [&](int t) {                        // KPI keys x 8 dims -> Vt
     if (!v_item) return;
     uint16_t* vt = reinterpret_cast<uint16_t*>(smem + (t % kStages) * Geo::STAGE + Geo::K_BYTES);
-    const int pos = 4 * vt_quad_pos(v_kp >> 1) + 2 * (v_kp & 1);
+    if constexpr (KPI == 2) {
+      const int pos = 4 * vt_quad_pos(v_kg >> 1) + 2 * (v_kg & 1);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {                     // dims 2w, 2w+1 of the chunk
-      const uint32_t lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-      const uint32_t hi = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-      *reinterpret_cast<uint32_t*>(&vt[(v_c * 8 + 2 * w) * VROW + pos]) = lo;
-      *reinterpret_cast<uint32_t*>(&vt[(v_c * 8 + 2 * w + 1) * VROW + pos]) = hi;
+      for (int w = 0; w < 4; ++w) {                   // dims 2w, 2w+1 of the chunk
+        const uint32_t lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
+        *reinterpret_cast<uint32_t*>(&vt[(v_c * 8 + 2 * w) * VROW + pos]) = lo;
+        *reinterpret_cast<uint32_t*>(&vt[(v_c * 8 + 2 * w + 1) * VROW + pos]) = hi;
+      }
+    } else {
+      const int pos = 4 * vt_quad_pos(v_kg);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {                   // dims 2w, 2w+1 of 4 keys each
+        const uint32_t a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
+        const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+        const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+        *reinterpret_cast<u32x2_t*>(&vt[(v_c * 8 + 2 * w) * VROW + pos]) = lo;
+        *reinterpret_cast<u32x2_t*>(&vt[(v_c * 8 + 2 * w + 1) * VROW + pos]) = hi;
+      }
     }
   };
 
-  f32x16_t o[DT];
+  f32x16_t o[QB][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m = -INFINITY;
-  float lsum = 0.f;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][dt][r] = 0.f;
+  float m[QB], lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+  }
   const uint32_t ones = 0x3f803f80u;   // bf16 pair (1, 1)
 
   // Fragments of the 32-key half `kb` of the tile in stage `st`: K rows (A operand of
-  // S^T = K Q^T) and V^T rows (A operand of O^T += V^T P^T).  They are read ahead of
-  // their MFMAs so that LDS latency overlaps the softmax.
+  // S^T = K Q^T) and V^T rows (A operand of O^T += V^T P^T), read ahead of their MFMAs.
   auto read_k = [&](const uint8_t* st, int kb, bf16x8_t (&kf)[KS]) {
     const int t = kb * 32 + l32;
 #pragma unroll
@@ -206,28 +240,29 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
         vf[kk][dt] = *reinterpret_cast<const bf16x8_t*>(
             sv + ((dt * 32 + l32) * VROW + kb * 32 + kk * 16 + 8 * hh) * 2);
   };
-  auto qk = [&](const bf16x8_t (&kf)[KS], f32x16_t& s) {
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16_t{}, 0, 0, 0);
+  auto qk = [&](const bf16x8_t (&kf)[KS], int qb, f32x16_t& s) {
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[qb][0], f32x16_t{}, 0, 0, 0);
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qb][ks], s, 0, 0, 0);
   };
-  auto pv = [&](const bf16x8_t (&vf)[2][DT], const bf16x8_t (&pf)[2]) {
+  auto pv = [&](const bf16x8_t (&vf)[2][DT], int qb, const bf16x8_t (&pf)[2]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][dt], pf[kk], o[dt], 0, 0, 0);
+        o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][dt], pf[kk], o[qb][dt], 0, 0, 0);
   };
-  // Softmax of one half: mask (if needed), lazy max, P as bf16 in P.V key order.
-  // Masked halves are scaled before the mask is applied (cs = 1 afterwards) so that a
-  // zero softmax_scale cannot turn -inf into NaN; unmasked halves fold the scale into
-  // the exponent's FMA.
-  auto softmax = [&](f32x16_t& s, int k0h, bf16x8_t (&pf)[2]) {
-    const bool masked = (k0h + 31 > diag + wq0) || (k0h + 32 > lk);
+  // Softmax of one half of query block qb: mask (if needed), lazy max, P as bf16 in
+  // P.V key order.  Masked halves are scaled before the mask is applied (cs = 1
+  // afterwards) so that a zero softmax_scale cannot turn -inf into NaN; unmasked halves
+  // fold the scale into the exponent's FMA.
+  auto softmax = [&](f32x16_t& s, int k0h, int qb, bf16x8_t (&pf)[2]) {
+    const int qlo = wq0 + qb * 32;
+    const bool masked = (k0h + 31 > diag + qlo) || (k0h + 32 > lk);
     const float cs = masked ? 1.0f : scale_log2e;
     if (masked) {
-      const int qi = wq0 + l32;
+      const int qi = qlo + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0h + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -238,26 +273,44 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
 #pragma unroll
     for (int r = 1; r < 16; ++r) x = fmaxf(x, s[r]);
     const float mx = xor32_max(x) * cs;
-    if (__any(mx > m + kLazy)) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mn);
-      lsum *= alpha;
+    if (__any(mx > m[qb] + kLazy)) {
+      const float mn = fmaxf(m[qb], mx);
+      const float alpha = fast_exp2(m[qb] - mn);
+      lsum[qb] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-      m = mn;
+      for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha;
+      m[qb] = mn;
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4_t w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p0 = fast_exp2(fmaf(s[8 * kk + 2 * i], cs, -m));
-        const float p1 = fast_exp2(fmaf(s[8 * kk + 2 * i + 1], cs, -m));
+        const float p0 = fast_exp2(fmaf(s[8 * kk + 2 * i], cs, -m[qb]));
+        const float p1 = fast_exp2(fmaf(s[8 * kk + 2 * i + 1], cs, -m[qb]));
         w[i] = pack_bf16x2(p0, p1);
-        lsum = dot2_bf16(w[i], ones, lsum);
+        lsum[qb] = dot2_bf16(w[i], ones, lsum[qb]);
       }
       pf[kk] = __builtin_bit_cast(bf16x8_t, w);
     }
+  };
+  // One 32-key half for every query block: QK of all blocks first, then per block
+  // softmax and P.V, so that each block's softmax runs beside MFMAs of another block.
+  auto half = [&](const uint8_t* st, int kb, int k0h) {
+    bf16x8_t kf[KS], vf[2][DT], pf[2];
+    f32x16_t s[QB];
+    read_k(st, kb, kf);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (k0h < diag + min(wq0 + qb * 32 + 32, lq)) qk(kf, qb, s[qb]);
+    read_v(st, kb, vf);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (k0h < diag + min(wq0 + qb * 32 + 32, lq)) {   // this block sees some key of the half
+        softmax(s[qb], k0h, qb, pf);
+        pv(vf, qb, pf);
+      }
   };
 
   // ---- prologue: ids of tiles 0..2, tile 0 into stage 0 ----
@@ -281,50 +334,37 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     }
     const int k0 = t * kBK;
     const uint8_t* st = smem + (t % kStages) * Geo::STAGE;
-    if (k0 < wkend) {
-      // half 0, with half 0's V^T and half 1's K fragments read before its softmax
-      bf16x8_t kf0[KS], kf1[KS], vf[2][DT], pf[2];
-      f32x16_t s;
-      read_k(st, 0, kf0);
-      qk(kf0, s);
-      read_v(st, 0, vf);
-      read_k(st, 1, kf1);                         // always in bounds; unused if no half 1
-      __builtin_amdgcn_sched_barrier(0);
-      softmax(s, k0, pf);
-      pv(vf, pf);
-      if (k0 + 32 < wkend) {
-        qk(kf1, s);
-        read_v(st, 1, vf);
-        __builtin_amdgcn_sched_barrier(0);
-        softmax(s, k0 + 32, pf);
-        pv(vf, pf);
-      }
-    }
+#pragma unroll
+    for (int kb = 0; kb < kBK / 32; ++kb)
+      if (k0 + 32 * kb < wkend) half(st, kb, k0 + 32 * kb);
     wait_vmem_all();
     if (more) commit_v(t + 1);
     __syncthreads();
   }
 
   // ---- epilogue: O^T / l -> bf16 rows staged in LDS, then contiguous row writes ----
-  uint8_t* ost = smem + wave * 32 * Geo::OROW;
-  if (wq0 < lq) {
-    const float inv = 1.0f / xor32_sum(lsum);     // the two lane halves hold different keys
+  uint8_t* ost = smem + wave * WQ * Geo::OROW;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+  for (int qb = 0; qb < QB; ++qb) {
+    if (wq0 + qb * 32 < lq) {
+      const float inv = 1.0f / xor32_sum(lsum[qb]);   // the two lane halves hold different keys
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = dt * 32 + 8 * r4 + 4 * hh;
-        const u32x2_t w = {pack_bf16x2(o[dt][4 * r4 + 0] * inv, o[dt][4 * r4 + 1] * inv),
-                           pack_bf16x2(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(ost + l32 * Geo::OROW + d0 * 2) = w;
-      }
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = dt * 32 + 8 * r4 + 4 * hh;
+          const u32x2_t w = {pack_bf16x2(o[qb][dt][4 * r4 + 0] * inv, o[qb][dt][4 * r4 + 1] * inv),
+                             pack_bf16x2(o[qb][dt][4 * r4 + 2] * inv, o[qb][dt][4 * r4 + 3] * inv)};
+          *reinterpret_cast<u32x2_t*>(ost + (qb * 32 + l32) * Geo::OROW + d0 * 2) = w;
+        }
+    }
   }
   __syncthreads();
   if (wq0 < lq) {
     constexpr int RPI = 64 / CPR;                 // rows per 64-lane pass
     const int rr = lane / CPR, cc = lane % CPR;
 #pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
+    for (int i = 0; i < WQ / RPI; ++i) {
       const int row = i * RPI + rr;
       const int qi = wq0 + row;
       if (qi < lq) {
@@ -393,10 +433,11 @@ prefill_f32_kernel(const float* __restrict__ q, int64_t q_row,
 
 template <int D, int G>
 static hipError_t launch_bf16(const PrefillArgs& a, hipStream_t st) {
-  using Geo = PfGeom<D, G>;
+  constexpr int QB = 8 / NKV_PREFILL_QB >= G ? NKV_PREFILL_QB : 1;   // G must divide the waves
+  using Geo = PfGeom<D, G, QB>;
   const PagedArgs& p = a.p;
   const int qtiles = (a.max_seqlen_q + Geo::BQ - 1) / Geo::BQ;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3(p.num_seqs * p.num_kv_heads, qtiles),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, QB>), dim3(p.num_seqs * p.num_kv_heads, qtiles),
                      dim3(Geo::NT), 0, st, static_cast<const uint16_t*>(a.q), a.q_row_elems,
                      static_cast<const uint16_t*>(p.k_cache), static_cast<const uint16_t*>(p.v_cache),
                      a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,
