@@ -134,8 +134,9 @@ nkv_status_t nkv_paged_attn_prefill(const void* q, int64_t q_row_stride,
                                     void* out, void* stream);
 
 /*
- * Bytes of device workspace nkv_paged_attn_decode needs for these sizes (split-K
- * partial results).  Depends on the current device's compute-unit count.
+ * Bytes of device workspace nkv_paged_attn_decode needs for these sizes (partial
+ * results of sequences split over several workgroups).  Depends on the current
+ * device's compute-unit count.
  */
 size_t nkv_paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                             int32_t num_kv_heads, int32_t head_dim,
@@ -152,15 +153,17 @@ size_t nkv_paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_head
  *   context_lens  [num_seqs] int32, each in [1, max_blocks_per_seq*block_size].
  *   block_table   [num_seqs, max_blocks_per_seq] int32.
  *   out           [num_seqs, num_q_heads, head_dim] contiguous, dtype of q.
- *   workspace     device buffer of at least nkv_paged_attn_decode_workspace_size(...)
+  *   workspace     device buffer of at least nkv_paged_attn_decode_workspace_size(...)
  *                 bytes, 16-byte aligned (may be NULL when that size is 0); its
  *                 contents on entry do not matter.  Calls that share a workspace must
  *                 be ordered on one stream.
- *   Long contexts are split over several workgroups ("split-K"), each producing a
- *   partial (max, sum, weighted values) that a second kernel merges; splits depend
- *   only on logical positions, so results are bitwise reproducible and do not depend
- *   on which physical blocks hold the data.
- *   Supported: as for prefill (bf16 and fp32 both on the VALU path).
+ *   Work is split over workgroups by logical position: bf16 takes equal shares of
+ *   (sequence, KV head, 16-position) rounds per workgroup ("stream-K"), fp32 fixed
+ *   spans per sequence ("split-K").  A sequence cut by a split leaves partials (max,
+ *   sum, weighted values) that are merged in a fixed order, so results are bitwise
+ *   reproducible and do not depend on which physical blocks hold the data.  A second
+ *   kernel merges the partials.
+ *   Supported: as for prefill; bf16 uses MFMA, fp32 the VALU.
  */
 nkv_status_t nkv_paged_attn_decode(const void* q,
                                    const void* k_cache, const void* v_cache,

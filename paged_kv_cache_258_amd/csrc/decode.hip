@@ -236,10 +236,13 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   }
   if (w == 0)
     for (int i = lane; i <= num_seqs; i += 64) ws_prefix[i] = s_prefix[i];
+  // Workers actually used: never more than there are rounds, so that every range is
+  // non-empty (the grid is sized from an upper bound on the lengths).
   const int64_t R = int64_t(hkv) * s_prefix[num_seqs];
-  const int64_t t0 = int64_t(w) * R / W;
-  const int64_t t1 = int64_t(w + 1) * R / W;
-  if (t0 >= t1) return;
+  const int We = R < W ? int(R) : W;
+  if (w >= We) return;
+  const int64_t t0 = int64_t(w) * R / We;
+  const int64_t t1 = int64_t(w + 1) * R / We;
 
   // ---- lookahead windows: lane i describes round wbase + i ----
   auto fill = [&](int64_t wbase, int slot, SkWin& wn) {
@@ -464,10 +467,11 @@ decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_
   const int64_t R = int64_t(num_kv_heads) * prefix[num_seqs];
   const int nr = prefix[b + 1] - prefix[b];
   if (nr == 0 || R == 0) return;
+  const int We = R < W ? int(R) : W;             // workers that had rounds, as above
   const int64_t s = int64_t(num_kv_heads) * prefix[b] + int64_t(g) * nr;   // first round
   const int64_t e = s + nr;                                               // past the last
-  // workgroup whose range holds round t: largest w with floor(w R / W) <= t
-  auto owner = [&](int64_t t) { return int(((t + 1) * W - 1) / R); };
+  // workgroup whose range holds round t: largest w with floor(w R / We) <= t
+  auto owner = [&](int64_t t) { return int(((t + 1) * We - 1) / R); };
   const int w0 = owner(s), w1 = owner(e - 1);
   if (w0 == w1) return;                      // finished in place
   // Lane i handles pieces i, i+64, ...: their (m, l) loads are independent, and the
@@ -475,7 +479,7 @@ decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_
   const int lane = threadIdx.x;
   const int np = w1 - w0 + 1;
   auto slot_of = [&](int w) {
-    const int k = (int64_t(w) * R / W >= s) ? 0 : 1;
+    const int k = (int64_t(w) * R / We >= s) ? 0 : 1;
     return (w * 2 + k) * G + col;
   };
   float M = -INFINITY;
