@@ -115,6 +115,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = g * G + wave % G;
+  if (wave < 4) __builtin_amdgcn_s_setprio(3);   // waves 0-3 lead their SIMD partners
   const int hq = G * num_kv_heads;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
