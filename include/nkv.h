@@ -39,6 +39,15 @@
  * with 0 <= Lq <= Lk per sequence.  A launch failure returns NKV_ERR_HIP.
  * nkv_last_error() gives a human-readable reason for the last failure on the
  * calling thread.
+ *
+ * Checking mode: with NKV_VALIDATE=1 in the environment (read at every call) each
+ * call first checks those device-resident preconditions on the device -- slots in
+ * range and unique, the block ids each sequence uses in [0, num_blocks),
+ * context_lens in [1, max_blocks_per_seq*block_size], cu_seqlens running sums from 0
+ * with Lq <= Lk, Lq <= max_seqlen_q, Lk <= max_seqlen_k and cu_seqlens_q[B] = total_q
+ * -- waits for the stream, and returns NKV_ERR_INVALID_ARG (naming the violation and
+ * the first offending token or sequence) without launching the operation.  It
+ * allocates nothing but synchronises the stream: a debugging aid, not for hot loops.
  */
 #ifndef NKV_H
 #define NKV_H

@@ -5,6 +5,7 @@
 // 「Nano-vLLM深度解读（下）」 §4, which only tests for slot == -1).
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -113,6 +114,29 @@ nkv_status_t check_paged(const void* k_cache, const void* v_cache, const int32_t
   return NKV_OK;
 }
 
+// Checking mode: NKV_VALIDATE=1 in the environment (read at every call).
+bool validating() {
+  const char* v = getenv("NKV_VALIDATE");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+const char* violation_name(int mask) {
+  if (mask & nkv::kValidateSlotRange) return "slot_mapping entry outside [-1, num_blocks*block_size)";
+  if (mask & nkv::kValidateSlotDuplicate) return "slot_mapping entry repeated in one call";
+  if (mask & nkv::kValidateSeqlens) return "cu_seqlens not running sums within max_seqlen / total_q";
+  if (mask & nkv::kValidateBlockId) return "block_table id outside [0, num_blocks)";
+  if (mask & nkv::kValidateContextLen) return "context_lens entry outside [1, max_blocks_per_seq*block_size]";
+  return "unknown violation";
+}
+
+nkv_status_t checked(hipError_t e, const nkv::ValidateResult& r, const char* what) {
+  if (e != hipSuccess) return fail(NKV_ERR_HIP, "%s check: %s", what, hipGetErrorString(e));
+  if (r.mask != 0)
+    return fail(NKV_ERR_INVALID_ARG, "%s (first at index %d; violation mask 0x%x)",
+                violation_name(r.mask), r.index, r.mask);
+  return NKV_OK;
+}
+
 }  // namespace
 
 NKV_EXPORT int nkv_abi_version(void) { return NKV_ABI_VERSION; }
@@ -158,6 +182,13 @@ NKV_EXPORT nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_strid
     return fail(NKV_ERR_INVALID_ARG, "key/value/cache pointers must be 16-byte aligned");
   nkv::StoreArgs a{key, key_row_stride * eb, value, value_row_stride * eb, k_cache, v_cache,
                    slot_mapping, num_tokens, row * eb, num_cus()};
+  if (validating()) {
+    nkv::ValidateResult r{};
+    const hipError_t e = nkv::validate_store(slot_mapping, num_tokens, int64_t(num_blocks) * block_size,
+                                             static_cast<hipStream_t>(stream), &r);
+    const nkv_status_t vs = checked(e, r, "nkv_store_kvcache");
+    if (vs != NKV_OK) return vs;
+  }
   return hip_status(nkv::launch_store(a, static_cast<hipStream_t>(stream)), "store launch");
 }
 
@@ -193,6 +224,12 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_prefill(
   a.max_seqlen_q = max_seqlen_q;
   a.max_seqlen_k = max_seqlen_k;
   a.out = out;
+  if (validating()) {
+    nkv::ValidateResult r{};
+    const hipError_t e = nkv::validate_prefill(a, total_q, num_blocks, static_cast<hipStream_t>(stream), &r);
+    const nkv_status_t vs = checked(e, r, "nkv_paged_attn_prefill");
+    if (vs != NKV_OK) return vs;
+  }
   return hip_status(nkv::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
@@ -234,5 +271,11 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_decode(
   a.context_lens = context_lens;
   a.out = out;
   a.workspace = workspace;
+  if (validating()) {
+    nkv::ValidateResult r{};
+    const hipError_t e = nkv::validate_decode(a, num_blocks, static_cast<hipStream_t>(stream), &r);
+    const nkv_status_t vs = checked(e, r, "nkv_paged_attn_decode");
+    if (vs != NKV_OK) return vs;
+  }
   return hip_status(nkv::launch_decode(a, plan, static_cast<hipStream_t>(stream)), "decode launch");
 }

@@ -77,6 +77,25 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                        int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                        int num_cus);
 
+// Checking mode: violation bits and the first offending index (token or sequence).
+enum : int {
+  kValidateSlotRange = 1,       // slot not -1 and outside [0, num_blocks*block_size)
+  kValidateSlotDuplicate = 2,   // a non-negative slot appears twice in one call
+  kValidateSeqlens = 4,         // cu_seqlens not running sums / lengths out of bounds
+  kValidateBlockId = 8,         // a used block_table entry outside [0, num_blocks)
+  kValidateContextLen = 16,     // context_lens[b] outside [1, max_blocks_per_seq*block_size]
+};
+struct ValidateResult {
+  int mask;
+  int index;
+};
+hipError_t validate_store(const int32_t* slots, int32_t n, int64_t rows, hipStream_t st,
+                          ValidateResult* r);
+hipError_t validate_prefill(const PrefillArgs& a, int32_t total_q, int32_t num_blocks,
+                            hipStream_t st, ValidateResult* r);
+hipError_t validate_decode(const DecodeArgs& a, int32_t num_blocks, hipStream_t st,
+                           ValidateResult* r);
+
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
