@@ -163,12 +163,28 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     k_row[j] = s / CPR;
     k_elem[j] = ((s % CPR) ^ (k_row[j] & (CPR - 1))) * 8;
   }
+  // With block_size >= kBK a tile lies inside one physical block: its base is uniform
+  // (one LDS read, scalar math) and each lane adds only row * row_elems.
+  const bool tile_in_block = log2_bs >= kLog2BK;
+  auto tile_base = [&](int t, const uint16_t* base) {
+    const int phys = __builtin_amdgcn_readfirstlane(s_ids[t % 3][0]);
+    return base + ((int64_t(phys) << log2_bs) + ((t * kBK) & bs_mask)) * row_elems;
+  };
   auto issue_k = [&](int t) {
     uint8_t* sk = smem + (t % kStages) * Geo::STAGE;
+    const int rmax = lk - 1 - t * kBK;               // rows past the keys repeat the last
+    if (tile_in_block) {
+      const uint16_t* tb = tile_base(t, kbase);
 #pragma unroll
-    for (int j = 0; j < Geo::K_DMA; ++j) {
-      const int key = min(t * kBK + k_row[j], lk - 1);
-      load_lds16(kbase + row_off(t, key) + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
+      for (int j = 0; j < Geo::K_DMA; ++j)
+        load_lds16(tb + min(k_row[j], rmax) * row_elems + k_elem[j],
+                   sk + (wave * Geo::K_DMA + j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < Geo::K_DMA; ++j) {
+        const int key = t * kBK + min(k_row[j], rmax);
+        load_lds16(kbase + row_off(t, key) + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
+      }
     }
   };
   constexpr int KPI = Geo::KPI;
@@ -176,12 +192,23 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int v_kg = tid % (kBK / KPI), v_c = tid / (kBK / KPI);   // key group, 16-byte chunk
   u32x4_t vreg[KPI];
   auto load_v = [&](int t) {
+    if (tile_in_block) {
+      const uint16_t* tb = tile_base(t, vbase) + v_c * 8;
 #pragma unroll
-    for (int j = 0; j < KPI; ++j) {
-      const int key = t * kBK + KPI * v_kg + j;
-      vreg[j] = (v_item && key < lk)                  // rows past the keys are zero, not NaN
-                    ? *reinterpret_cast<const u32x4_t*>(vbase + row_off(t, key) + v_c * 8)
-                    : u32x4_t{0, 0, 0, 0};
+      for (int j = 0; j < KPI; ++j) {
+        const int r = KPI * v_kg + j;
+        vreg[j] = (v_item && t * kBK + r < lk)        // rows past the keys are zero, not NaN
+                      ? *reinterpret_cast<const u32x4_t*>(tb + r * row_elems)
+                      : u32x4_t{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPI; ++j) {
+        const int key = t * kBK + KPI * v_kg + j;
+        vreg[j] = (v_item && key < lk)
+                      ? *reinterpret_cast<const u32x4_t*>(vbase + row_off(t, key) + v_c * 8)
+                      : u32x4_t{0, 0, 0, 0};
+      }
     }
   };
   auto commit_v = [&](int t) {                        // KPI keys x 8 dims -> Vt
