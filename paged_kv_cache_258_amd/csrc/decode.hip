@@ -178,6 +178,50 @@ struct SkGeom {
       (kSkStages - 1) * LOADS < 63 ? (kSkStages - 1) * LOADS : 63;
 };
 
+// How the R rounds of a launch are cut into pieces.  The first Rs rounds are split
+// evenly over We persistent workgroups (stream-K); when every workgroup has enough
+// rounds, the last ~15% are cut into U units of L rounds that workgroups claim from a
+// counter once their own range is done, so that faster CUs take more of the tail.
+// Piece p: p < We is workgroup p's range, p >= We is unit p - We.  The cuts depend
+// only on R and the grid, never on timing, so the merge order of partials is fixed.
+#ifndef NKV_SK_DYN_NUM
+#define NKV_SK_DYN_NUM 3              // twentieths of the rounds handed out as units
+#endif
+#ifndef NKV_SK_UNIT_MIN
+#define NKV_SK_UNIT_MIN 16
+#endif
+constexpr int kSkDynMinPerWg = 32;    // rounds per workgroup below which no units
+constexpr int kSkDynNum = NKV_SK_DYN_NUM, kSkDynDen = 20;
+constexpr int kSkUnitMin = NKV_SK_UNIT_MIN;   // rounds per unit, at least
+constexpr int kSkMaxUnits = 4096;     // units per launch, at most (workspace slots)
+
+struct SkSplit {
+  int64_t R, Rs;
+  int We, L, U;
+  __device__ int64_t start(int p) const {
+    return p < We ? int64_t(p) * Rs / We : Rs + int64_t(p - We) * L;
+  }
+  __device__ int64_t end(int p) const {
+    const int64_t e = start(p + 1);
+    return e < R ? e : R;
+  }
+  __device__ int piece(int64_t t) const {    // piece that holds round t
+    return t < Rs ? int(((t + 1) * We - 1) / Rs) : We + int((t - Rs) / L);
+  }
+};
+
+__device__ __forceinline__ SkSplit make_split(int64_t R, int W) {
+  SkSplit sp;
+  sp.R = R;
+  sp.We = R < W ? int(R) : W;               // every static range non-empty
+  const int64_t Rd = R >= int64_t(kSkDynMinPerWg) * sp.We ? R * kSkDynNum / kSkDynDen : 0;
+  const int64_t L = Rd > 0 ? (Rd + kSkMaxUnits - 1) / kSkMaxUnits : kSkUnitMin;
+  sp.L = int(L > kSkUnitMin ? L : kSkUnitMin);
+  sp.U = int((Rd + sp.L - 1) / sp.L);
+  sp.Rs = R - Rd;
+  return sp;
+}
+
 // Descriptor of round t (per lane of a window): which pair, where, how long.
 struct SkWin {
   int b;      // sequence
@@ -194,7 +238,7 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       int32_t num_seqs, int32_t num_kv_heads, int32_t log2_bs,
                       float scale_log2e, uint16_t* __restrict__ out,
                       float* __restrict__ ws_part, float* __restrict__ ws_ml,
-                      int32_t* __restrict__ ws_prefix) {
+                      int32_t* __restrict__ ws_prefix, int32_t* __restrict__ ws_claim) {
   using Geo = SkGeom<D, G>;
   using Row = typename Geo::Row;
   constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
@@ -239,10 +283,13 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // Workers actually used: never more than there are rounds, so that every range is
   // non-empty (the grid is sized from an upper bound on the lengths).
   const int64_t R = int64_t(hkv) * s_prefix[num_seqs];
-  const int We = R < W ? int(R) : W;
-  if (w >= We) return;
-  const int64_t t0 = int64_t(w) * R / We;
-  const int64_t t1 = int64_t(w + 1) * R / We;
+  const SkSplit sp = make_split(R, W);
+  if (w >= sp.We) return;
+  // The unit counter starts at zero: zeroed here, long before any workgroup finishes
+  // its own range and claims, and again by the fixup kernel after every launch.
+  if (w == 0 && lane == 0 && sp.U > 0) atomicExch(ws_claim, 0);
+  int64_t t0 = sp.start(w), t1 = sp.end(w);  // the range being processed
+  int piece = w;                              // its partial slots
 
   // ---- lookahead windows: lane i describes round wbase + i ----
   auto fill = [&](int64_t wbase, int slot, SkWin& wn) {
@@ -265,10 +312,6 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   SkWin wa, wb;
   int64_t wbase = t0;        // window slot `wcur` covers [wbase, wbase + 64)
   int wcur = 0;
-  fill(wbase, 0, wa);
-  fill(wbase + kSkWindow, 1, wb);
-  wait_vmcnt<0>();  // the first windows are read right away; later fills land within
-                    // two rounds, long before the issue cursor reaches them
 
   struct Desc {
     int b, g, local, nr, len, phys;
@@ -326,9 +369,6 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
   };
 
-#pragma unroll
-  for (int i = 0; i < kSkStages - 1; ++i)
-    if (t0 + i < t1) issue(t0 + i);
 
   // ---- per-lane LDS offsets: K rows (A operand), V^T (transposing reads) ----
   const int col = lane & 15;        // MFMA column = head inside the group
@@ -353,6 +393,17 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   int seg_local0 = 0;
   bool seg_first = true;
 
+  // ---- one range [t0, t1): windows, ring prologue, rounds ----
+  auto run_range = [&]() {
+  wbase = t0;
+  wcur = 0;
+  fill(wbase, 0, wa);
+  fill(wbase + kSkWindow, 1, wb);
+  wait_vmcnt<0>();  // the first windows are read right away; later fills land within
+                    // two rounds, long before the issue cursor reaches them
+#pragma unroll
+  for (int i = 0; i < kSkStages - 1; ++i)
+    if (t0 + i < t1) issue(t0 + i);
   for (int64_t c = t0; c < t1; ++c) {
     if (c - wbase == kSkWindow) {           // slide the lookahead windows
       wbase += kSkWindow;
@@ -437,7 +488,7 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             *reinterpret_cast<u32x2_t*>(out + row * D + dt * 16 + 4 * quad) = wv;
           }
         } else {                                          // a piece: partial for the fixup
-          const int64_t slot = (int64_t(w) * 2 + (seg_first ? 0 : 1)) * G + col;
+          const int64_t slot = (int64_t(piece) * 2 + (seg_first ? 0 : 1)) * G + col;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
             *reinterpret_cast<f32x4_t*>(ws_part + slot * D + dt * 16 + 4 * quad) = o[dt];
@@ -449,37 +500,54 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
     }
   }
+  };
+
+  run_range();                                 // this workgroup's own range
+  // Then units of the tail, claimed one at a time.  The copy ring is drained at the end
+  // of every range, so waiting for the claim costs no overlap.
+  for (;;) {
+    if (sp.U == 0) break;
+    int u = 0;
+    if (lane == 0) u = atomicAdd(ws_claim, 1);
+    u = __builtin_amdgcn_readfirstlane(u);
+    // unsigned: a counter value not yet reset (workspace contents on entry are
+    // arbitrary) never names a piece; workgroup 0 resets it and then claims until done
+    if (unsigned(u) >= unsigned(sp.U)) break;
+    piece = sp.We + u;
+    t0 = sp.start(piece);
+    t1 = sp.end(piece);
+    run_range();
+  }
 }
 
-// Merge the pieces of every pair that a range boundary cut.  Piece of workgroup w:
-// slot 0 if the pair is w's first piece (w's range starts inside or at the start of
-// the pair), else slot 1 (the pair is w's last piece).
+// Merge the pieces of every pair that a piece boundary cut.  Piece p holds the pair in
+// slot 0 if p's range starts inside or at the start of the pair (the pair is p's first
+// segment), else in slot 1 (the pair is p's last segment).
 template <int D, int G>
 __global__ void __launch_bounds__(64)
 decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_t num_kv_heads,
                     int32_t W, const float* __restrict__ ws_part, const float* __restrict__ ws_ml,
-                    uint16_t* __restrict__ out) {
+                    int32_t* __restrict__ ws_claim, uint16_t* __restrict__ out) {
   constexpr int DPT = D / 64;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int g = h / G;
   const int col = h % G;
+  if (h == 0 && b == 0 && threadIdx.x == 0) atomicExch(ws_claim, 0);   // for the next launch
   const int64_t R = int64_t(num_kv_heads) * prefix[num_seqs];
   const int nr = prefix[b + 1] - prefix[b];
   if (nr == 0 || R == 0) return;
-  const int We = R < W ? int(R) : W;             // workers that had rounds, as above
+  const SkSplit sp = make_split(R, W);           // the stream-K kernel's pieces
   const int64_t s = int64_t(num_kv_heads) * prefix[b] + int64_t(g) * nr;   // first round
   const int64_t e = s + nr;                                               // past the last
-  // workgroup whose range holds round t: largest w with floor(w R / We) <= t
-  auto owner = [&](int64_t t) { return int(((t + 1) * We - 1) / R); };
-  const int w0 = owner(s), w1 = owner(e - 1);
+  const int w0 = sp.piece(s), w1 = sp.piece(e - 1);
   if (w0 == w1) return;                      // finished in place
   // Lane i handles pieces i, i+64, ...: their (m, l) loads are independent, and the
   // partial rows are then summed in piece order with many loads in flight.
   const int lane = threadIdx.x;
   const int np = w1 - w0 + 1;
   auto slot_of = [&](int w) {
-    const int k = (int64_t(w) * R / We >= s) ? 0 : 1;
+    const int k = sp.start(w) >= s ? 0 : 1;
     return (w * 2 + k) * G + col;
   };
   float M = -INFINITY;
@@ -802,10 +870,14 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   if (wgs > max_rounds) wgs = max_rounds;
   if (wgs < 1) wgs = 1;
   p.wgs = int32_t(wgs);
+  // partial slots: one pair of slots per workgroup range, plus per tail unit when the
+  // rounds can reach kSkDynMinPerWg per workgroup (the kernel's own condition)
+  p.pieces = p.wgs + (max_rounds >= int64_t(kSkDynMinPerWg) * p.wgs ? kSkMaxUnits : 0);
   const size_t ws_bf16 = num_seqs <= 0 ? 0
-                                       : align16(size_t(p.wgs) * 2 * grp * head_dim * sizeof(float)) +
-                                             align16(size_t(p.wgs) * 2 * grp * 2 * sizeof(float)) +
-                                             align16(size_t(p.seq_chunk + 1) * sizeof(int32_t));
+                                       : align16(size_t(p.pieces) * 2 * grp * head_dim * sizeof(float)) +
+                                             align16(size_t(p.pieces) * 2 * grp * 2 * sizeof(float)) +
+                                             align16(size_t(p.seq_chunk + 1) * sizeof(int32_t)) +
+                                             16;   // the unit counter
   p.workspace_bytes = ws_f32 > ws_bf16 ? ws_f32 : ws_bf16;
   return p;
 }
@@ -815,9 +887,11 @@ static hipError_t launch_bf16_t(const DecodeArgs& a, const DecodePlan& plan, hip
   const PagedArgs& p = a.p;
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   float* ws_part = reinterpret_cast<float*>(ws);
-  float* ws_ml = reinterpret_cast<float*>(ws + align16(size_t(plan.wgs) * 2 * G * D * sizeof(float)));
+  float* ws_ml = reinterpret_cast<float*>(ws + align16(size_t(plan.pieces) * 2 * G * D * sizeof(float)));
   int32_t* ws_prefix = reinterpret_cast<int32_t*>(
-      reinterpret_cast<uint8_t*>(ws_ml) + align16(size_t(plan.wgs) * 2 * G * 2 * sizeof(float)));
+      reinterpret_cast<uint8_t*>(ws_ml) + align16(size_t(plan.pieces) * 2 * G * 2 * sizeof(float)));
+  int32_t* ws_claim = reinterpret_cast<int32_t*>(
+      reinterpret_cast<uint8_t*>(ws_prefix) + align16(size_t(plan.seq_chunk + 1) * sizeof(int32_t)));
   const int64_t row = int64_t(p.num_q_heads) * D;
   for (int32_t c0 = 0; c0 < p.num_seqs; c0 += plan.seq_chunk) {
     const int32_t n = p.num_seqs - c0 < plan.seq_chunk ? p.num_seqs - c0 : plan.seq_chunk;
@@ -828,11 +902,11 @@ static hipError_t launch_bf16_t(const DecodeArgs& a, const DecodePlan& plan, hip
     hipLaunchKernelGGL((decode_streamk_kernel<D, G>), dim3(plan.wgs), dim3(64), 0, st, q,
                        static_cast<const uint16_t*>(p.k_cache), static_cast<const uint16_t*>(p.v_cache),
                        lens, table, p.max_blocks_per_seq, n, p.num_kv_heads, p.log2_block_size,
-                       p.scale_log2e, out, ws_part, ws_ml, ws_prefix);
+                       p.scale_log2e, out, ws_part, ws_ml, ws_prefix, ws_claim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_fixup_kernel<D, G>), dim3(p.num_q_heads, n), dim3(64), 0, st,
-                       ws_prefix, n, p.num_kv_heads, plan.wgs, ws_part, ws_ml, out);
+                       ws_prefix, n, p.num_kv_heads, plan.wgs, ws_part, ws_ml, ws_claim, out);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -69,6 +69,7 @@ struct DecodePlan {
   int32_t split_tokens;
   int32_t max_splits;
   int32_t wgs;
+  int32_t pieces;           // stream-K partial-slot pairs: wgs ranges + tail units
   int32_t seq_chunk;
   size_t workspace_bytes;
 };

@@ -194,3 +194,30 @@ def test_decode_workspace_reused_across_calls_and_dtypes():
     for i in (2, 3, 5):
         assert np.array_equal(outs[i], outs[0]), f"bf16 call {i} differs from the first"
     assert np.array_equal(outs[4], outs[1])
+
+
+@pytest.mark.parametrize("wgs", ["3", "37", "150"])
+def test_decode_tail_units_claimed_in_any_order(wgs, monkeypatch):
+    # With few workgroups every one has many rounds, so the last rounds are handed out
+    # as units through a counter.  Whichever workgroup claims a unit, its partials land
+    # in the unit's own slots and are merged in round order: the result must match the
+    # oracle and repeat bitwise, also when the counter holds garbage on entry.
+    monkeypatch.setenv("NKV_DECODE_WORKGROUPS", wgs)
+    dev = require_gpu()
+    case = random_case(500 + int(wgs), [4096, 3001, 2048, 777, 300, 63, 1, 129, 2500, 1000],
+                       wl.QWEN3_8B)
+    check(case, f"tail units, {wgs} workgroups")
+    need = nkv_paged_attn_decode_workspace_size(len(case.context_lens), 32, 8, 128,
+                                                 case.block_table.shape[1], 256)
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    nkv_store_kvcache(case.k, case.v, kc, vc, dev_i32(case.slot_mapping, dev))
+    lens, table = dev_i32(case.context_lens, dev), dev_i32(case.block_table, dev)
+    outs = []
+    for fill in (0x00, 0x80, 0x7F, 0x00):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=dev)
+        outs.append(nkv_paged_attn_decode(case.q, kc, vc, lens, table, case.shape.scale,
+                                          workspace=ws))
+    torch.cuda.synchronize()
+    for i in range(1, len(outs)):
+        assert torch.equal(outs[i].view(torch.int16), outs[0].view(torch.int16)), \
+            f"call {i} differs bitwise"
