@@ -33,11 +33,13 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
-# Per-source flags.  prefill.hip: keep MFMA accumulators and results in VGPRs; with
-# the default heuristic the O^T accumulators live in AGPRs and every loop iteration
-# copies all of them to VGPRs and back around the (rarely taken) rescale branch.
+# Per-source flags.  prefill.hip, decode.hip: keep MFMA accumulators and results in
+# VGPRs; with the default heuristic the O^T accumulators live in AGPRs and every loop
+# iteration copies all of them between AGPRs (and to VGPRs and back around the rarely
+# taken rescale branch).
 SOURCE_FLAGS = {
     "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -115,6 +115,13 @@ __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "v"(gptr), "s"(lds_addr(lds_base)) : "memory");
 }
+// Same copy with the address split into a wave-uniform 64-bit base (SGPRs) and a 32-bit
+// per-lane byte offset: no 64-bit address arithmetic per lane.
+__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, void* lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_addr(lds_base)) : "memory");
+}
 __device__ __forceinline__ void load_lds4(const void* gptr, void* lds_base) {
   uint32_t saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"

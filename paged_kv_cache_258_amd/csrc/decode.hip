@@ -173,9 +173,11 @@ struct SkGeom {
   static constexpr int QI = (G * QROW + 1023) / 1024;      // q copy instructions per round
   static constexpr int QSLOT = QI * 1024;
   static constexpr int STAGE = 2 * Row::ROUND_BYTES + QSLOT;  // K, V, q
-  static constexpr int LOADS = 2 * Row::LPR + QI;           // copies per round
+  static constexpr int KV_LOADS = 2 * Row::LPR;             // K and V copies of every round
+  // q is copied only with the first round of a piece of a pair, so a round has KV_LOADS
+  // or KV_LOADS + QI copies; waiting as if every round had KV_LOADS is exact or stricter
   static constexpr int IN_FLIGHT =
-      (kSkStages - 1) * LOADS < 63 ? (kSkStages - 1) * LOADS : 63;
+      (kSkStages - 1) * KV_LOADS < 63 ? (kSkStages - 1) * KV_LOADS : 63;
 };
 
 // How the R rounds of a launch are cut into pieces.  The first Rs rounds are split
@@ -324,14 +326,14 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       d.b = __builtin_amdgcn_readlane(wa.b, idx);
       gl = __builtin_amdgcn_readlane(wa.gl, idx);
       d.nr = __builtin_amdgcn_readlane(wa.nr, idx);
-      d.len = s_len[wcur][idx];
-      d.phys = s_phys[wcur][idx];
+      d.len = __builtin_amdgcn_readfirstlane(s_len[wcur][idx]);
+      d.phys = __builtin_amdgcn_readfirstlane(s_phys[wcur][idx]);
     } else {
       d.b = __builtin_amdgcn_readlane(wb.b, idx - kSkWindow);
       gl = __builtin_amdgcn_readlane(wb.gl, idx - kSkWindow);
       d.nr = __builtin_amdgcn_readlane(wb.nr, idx - kSkWindow);
-      d.len = s_len[wcur ^ 1][idx - kSkWindow];
-      d.phys = s_phys[wcur ^ 1][idx - kSkWindow];
+      d.len = __builtin_amdgcn_readfirstlane(s_len[wcur ^ 1][idx - kSkWindow]);
+      d.phys = __builtin_amdgcn_readfirstlane(s_phys[wcur ^ 1][idx - kSkWindow]);
     }
     d.g = gl & 0xff;
     d.local = gl >> 8;
@@ -339,35 +341,57 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   };
 
   // ---- copies of one round: K and V rows into the stage, plus the pair's q ----
+  // Lane offsets in bytes are fixed for the whole launch: row lrow[j] of the round, the
+  // swizzled 16-byte chunk of that row; the round itself is a wave-uniform base address.
+  const int row_bytes = hkv * D * 2;                  // one pool row (all KV heads)
   int lrow[Row::LPR], lelem[Row::LPR];
+  uint32_t voff[Row::LPR];
 #pragma unroll
   for (int j = 0; j < Row::LPR; ++j) {
     const int s = j * 64 + lane;
     lrow[j] = s / Row::CPR;
     lelem[j] = ((s % Row::CPR) ^ (lrow[j] & (Row::CPR - 1))) * Row::EPV;
+    voff[j] = uint32_t(lrow[j] * row_bytes + lelem[j] * 2);
   }
-  auto issue = [&](int64_t t) {
-    const Desc d = desc(t);
+  uint32_t qoff[Geo::QI];
+#pragma unroll
+  for (int j = 0; j < Geo::QI; ++j) {
+    const int ch = j * 64 + lane;
+    const int head = min(ch / Geo::QCH, G - 1);
+    qoff[j] = uint32_t((head * D + (ch % Geo::QCH) * 8) * 2);
+  }
+  auto issue = [&](int64_t t, const Desc& d) {
     uint8_t* sk = ring + int((t - t0) % kSkStages) * Geo::STAGE;
     uint8_t* sv = sk + Row::ROUND_BYTES;
     uint8_t* sq = sv + Row::ROUND_BYTES;
     const int base = d.local * kRound;
-    const int64_t blk0 = int64_t(d.phys) << log2_bs;
-    const int64_t row_elems = int64_t(hkv) * D;
+    // the 16 positions of a round lie in one block (block_size >= 16, rounds aligned)
+    const int64_t off = ((int64_t(d.phys) << log2_bs) + (base & bs_mask)) * row_bytes +
+                        int64_t(d.g) * (D * 2);
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(k_cache) + off;
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(v_cache) + off;
+    if (base + kRound <= d.len) {
 #pragma unroll
-    for (int j = 0; j < Row::LPR; ++j) {
-      const int pos = min(base + lrow[j], d.len - 1);
-      const int64_t off = (blk0 + (pos & bs_mask)) * row_elems + int64_t(d.g) * D + lelem[j];
-      load_lds16(k_cache + off, sk + j * 1024);
-      load_lds16(v_cache + off, sv + j * 1024);
+      for (int j = 0; j < Row::LPR; ++j) {
+        load_lds16_s(kb, voff[j], sk + j * 1024);
+        load_lds16_s(vb, voff[j], sv + j * 1024);
+      }
+    } else {             // the sequence ends inside this round: rows past it repeat the last
+      const int last = d.len - 1 - base;
+#pragma unroll
+      for (int j = 0; j < Row::LPR; ++j) {
+        const uint32_t o = uint32_t(min(lrow[j], last) * row_bytes + lelem[j] * 2);
+        load_lds16_s(kb, o, sk + j * 1024);
+        load_lds16_s(vb, o, sv + j * 1024);
+      }
     }
+    if (d.local == 0 || t == t0) {   // q is read only where a pair's piece starts
+      const uint8_t* qbase = reinterpret_cast<const uint8_t*>(q) + (int64_t(d.b) * hq + d.g * G) * (D * 2);
 #pragma unroll
-    for (int j = 0; j < Geo::QI; ++j) {
-      const int ch = j * 64 + lane;
-      const int head = min(ch / Geo::QCH, G - 1);
-      load_lds16(q + (int64_t(d.b) * hq + d.g * G + head) * D + (ch % Geo::QCH) * 8, sq + j * 1024);
+      for (int j = 0; j < Geo::QI; ++j) load_lds16_s(qbase, qoff[j], sq + j * 1024);
     }
   };
+  Desc dd[kSkStages];    // descriptors of the rounds in the ring, oldest first
 
 
   // ---- per-lane LDS offsets: K rows (A operand), V^T (transposing reads) ----
@@ -403,7 +427,10 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                     // two rounds, long before the issue cursor reaches them
 #pragma unroll
   for (int i = 0; i < kSkStages - 1; ++i)
-    if (t0 + i < t1) issue(t0 + i);
+    if (t0 + i < t1) {
+      dd[i] = desc(t0 + i);
+      issue(t0 + i, dd[i]);
+    }
   for (int64_t c = t0; c < t1; ++c) {
     if (c - wbase == kSkWindow) {           // slide the lookahead windows
       wbase += kSkWindow;
@@ -412,12 +439,15 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       fill(wbase + kSkWindow, wcur ^ 1, wb);
     }
     if (c + kSkStages - 1 < t1) {
-      issue(c + kSkStages - 1);
+      dd[kSkStages - 1] = desc(c + kSkStages - 1);
+      issue(c + kSkStages - 1, dd[kSkStages - 1]);
       wait_vmcnt<Geo::IN_FLIGHT>();         // round c has landed
     } else {
       wait_vmcnt<0>();
     }
-    const Desc d = desc(c);
+    const Desc d = dd[0];
+#pragma unroll
+    for (int i = 0; i + 1 < kSkStages; ++i) dd[i] = dd[i + 1];
     const uint8_t* sk = ring + int((c - t0) % kSkStages) * Geo::STAGE;
     const uint8_t* sv = sk + Row::ROUND_BYTES;
     const uint8_t* sq = sv + Row::ROUND_BYTES;
