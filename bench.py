@@ -19,8 +19,15 @@ traffic = HBM bytes per decode call measured by rocprofv3 counters (FETCH_SIZE a
 WRITE_SIZE, calibrated on a plain copy of known size), read from
 profiles/decode_c2_counters.json when it was taken on the current decode sources.
 cpu_baseline = the float64 CPU oracle (store_ref + decode_ref) on the same C2 batch.
+decode_call / prefill_call = mean, median and minimum of the per-call event times.
+Prefill legs are timed in steady state: after the warm-up calls, 10 calls are timed at once
+(cold_prefill_call), the matrix cores are then kept busy for settle_s seconds (the first
+tens of milliseconds of back-to-back MFMA work run slower while the engine clock
+settles), and only then are the `steps` reported calls timed.
+peaks = the spec peaks beside CUs x max engine clock x 4096 flop/clock (bf16 MFMA) from the
+device properties.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-prefill] [--no-c5]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu] [--no-prefill] [--no-c5]
 Prints ONE JSON line on stdout; progress goes to stderr.
 
 Counter collection (two rocprofv3 passes, then a summary written to profiles/):
@@ -54,6 +61,49 @@ DECODE_SOURCES = ["decode.hip", "common.hpp", "launch.hpp"]
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def stats_us(ms_list):
+    """Mean, median and minimum of per-call event times (ms) in microseconds."""
+    xs = sorted(ms_list)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"mean_us": round(1e3 * sum(xs) / n, 2), "median_us": round(1e3 * med, 2),
+            "min_us": round(1e3 * xs[0], 2)}
+
+
+def hold_stream(ms):
+    """Keep the GPU busy for about `ms` with a spin kernel, so that the host enqueues the
+    timed calls while the GPU is still busy and a host-side hiccup cannot open gaps
+    inside the timed region."""
+    import torch
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
+
+
+def device_peaks(props):
+    """Spec peaks beside the peaks implied by the device's own properties.
+
+    The bf16 MFMA rate of a CDNA4 CU is 4096 flop per clock (4 SIMDs x 1024), so the
+    device-derived peak is CUs x max engine clock x 4096.  The clock comes from the HIP
+    runtime (hipDeviceAttributeClockRate, kHz).
+    """
+    clock_khz = getattr(props, "clock_rate", None)
+    if not clock_khz:
+        try:
+            import ctypes
+            hip = ctypes.CDLL("libamdhip64.so")
+            v = ctypes.c_int(0)
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:   # ClockRate
+                clock_khz = v.value
+        except OSError:
+            clock_khz = None
+    cus = props.multi_processor_count
+    out = {"hbm_spec_gbs": HBM_PEAK_GBS, "mfma_bf16_spec_tflops": MFMA_BF16_PEAK_TFLOPS,
+           "cus": cus, "max_clock_mhz": round(clock_khz / 1e3, 1) if clock_khz else None,
+           "mfma_bf16_from_props_tflops":
+               round(cus * clock_khz * 1e3 * 4096 / 1e12, 1) if clock_khz else None}
+    return out
 
 
 def kernel_source_sha(files) -> str:
@@ -108,6 +158,7 @@ def bench_decode(dev, steps, warmup):
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    hold_stream(10.0)
     t0.record()
     for i in range(steps):
         step(i, evs[i])
@@ -117,16 +168,18 @@ def bench_decode(dev, steps, warmup):
     ms_step = t0.elapsed_time(t1) / steps
     store_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    dec_stats = stats_us([e[1].elapsed_time(e[2]) for e in evs])
+    store_stats = stats_us([e[0].elapsed_time(e[1]) for e in evs])
     dec_bytes = acc.decode_bytes(case.context_lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
                                  sh.block_size, sh.elem_bytes)
     st_bytes = acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
     log(f"[decode C2] step {ms_step*1e3:.1f} us (store {store_ms*1e3:.1f} us, decode "
         f"{dec_ms*1e3:.1f} us) -> decode {dec_bytes/dec_ms/1e6:.0f} GB/s, wall {wall:.3f}s")
     return dict(case=case, ms_step=ms_step, store_ms=store_ms, dec_ms=dec_ms, dec_bytes=dec_bytes,
-                st_bytes=st_bytes, workspace_bytes=need)
+                st_bytes=st_bytes, workspace_bytes=need, dec_stats=dec_stats, store_stats=store_stats)
 
 
-def bench_prefill(dev, which, steps, warmup):
+def bench_prefill(dev, which, steps, warmup, settle_s=0.25):
     import torch
     import paged_kv_cache_258_amd as nkv
     from paged_kv_cache_258_amd import accounting as acc
@@ -157,15 +210,30 @@ def bench_prefill(dev, which, steps, warmup):
         if ev is not None:
             ev[2].record()
 
+    def timed(n):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        hold_stream(10.0)
+        for i in range(n):
+            step(evs[i])
+        torch.cuda.synchronize()
+        return evs
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
+    # The first tens of milliseconds of back-to-back MFMA work run slower than the rest
+    # (the engine clock settles under the sustained load): time a few calls right away
+    # ("cold"), keep the matrix cores busy for settle_s, then time the steady state.
+    cold = stats_us([e[1].elapsed_time(e[2]) for e in timed(10)])
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    evs = timed(steps)
     store_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     pf_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    pf_stats = stats_us([e[1].elapsed_time(e[2]) for e in evs])
     flops = acc.prefill_flops(case.cu_seqlens_q, case.cu_seqlens_k, sh.num_q_heads, sh.head_dim)
     st_bytes = acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
     tflops = flops / pf_ms / 1e9
@@ -173,7 +241,8 @@ def bench_prefill(dev, which, steps, warmup):
         f"prefill {pf_ms*1e3:.1f} us -> {tflops:.1f} TFLOP/s")
     return {"workload": which, "prefill_us": round(pf_ms * 1e3, 2),
             "tflops": round(tflops, 2), "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "flop": flops, "store_us": round(store_ms * 1e3, 2),
+            "flop": flops, "prefill_call": pf_stats, "cold_prefill_call": cold,
+            "settle_s": settle_s, "store_us": round(store_ms * 1e3, 2),
             "store_gbs": round(st_bytes / store_ms / 1e6, 1)}
 
 
@@ -228,6 +297,7 @@ def bench_c5(dev, kind, reps, warmup):
         run_all()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_stream(10.0)
     e0.record()
     for _ in range(reps):
         run_all()
@@ -369,7 +439,7 @@ def summarize_counters(fetch_csv, write_csv):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill legs")
@@ -403,8 +473,8 @@ def main():
     d = bench_decode(dev, args.steps, args.warmup)
     prefill = []
     if not args.no_prefill:
-        prefill.append(bench_prefill(dev, "C3", max(5, args.steps // 2), 2))
-        prefill.append(bench_prefill(dev, "C4", max(5, args.steps // 2), 2))
+        prefill.append(bench_prefill(dev, "C3", args.steps, 2))
+        prefill.append(bench_prefill(dev, "C4", args.steps, 2))
     long_decode = []
     if not args.no_c5:
         for kind in ("a", "b"):
@@ -452,7 +522,9 @@ def main():
             "avg_launch_us": round(d["dec_ms"] * 1e3, 2),
             "kernel_source_sha": sha,
         },
-        "store": {"avg_launch_us": round(d["store_ms"] * 1e3, 2),
+        "decode_call": d["dec_stats"],
+        "peaks": device_peaks(props),
+        "store": {"avg_launch_us": round(d["store_ms"] * 1e3, 2), "call": d["store_stats"],
                   "gbs": round(d["st_bytes"] / d["store_ms"] / 1e6, 1)},
         "prefill": prefill,
         "long_decode": long_decode,

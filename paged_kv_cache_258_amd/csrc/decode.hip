@@ -192,7 +192,10 @@ struct SkGeom {
 #ifndef NKV_SK_UNIT_MIN
 #define NKV_SK_UNIT_MIN 16
 #endif
-constexpr int kSkDynMinPerWg = 32;    // rounds per workgroup below which no units
+#ifndef NKV_SK_DYN_MIN_PER_WG
+#define NKV_SK_DYN_MIN_PER_WG 32
+#endif
+constexpr int kSkDynMinPerWg = NKV_SK_DYN_MIN_PER_WG;   // rounds per workgroup below which no units
 constexpr int kSkDynNum = NKV_SK_DYN_NUM, kSkDynDen = 20;
 constexpr int kSkUnitMin = NKV_SK_UNIT_MIN;   // rounds per unit, at least
 constexpr int kSkMaxUnits = 4096;     // units per launch, at most (workspace slots)
@@ -553,17 +556,31 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 // Merge the pieces of every pair that a piece boundary cut.  Piece p holds the pair in
 // slot 0 if p's range starts inside or at the start of the pair (the pair is p's first
 // segment), else in slot 1 (the pair is p's last segment).
+//
+// One single-wave workgroup per (Q head, sequence); most of them find their pair whole and
+// leave at once.  Lane l owns the 16-byte column chunk l % (D/4) of the partial rows of
+// pieces l / (D/4), l / (D/4) + PG, ... of a chunk of kFixPieces pieces: all of a chunk's
+// row and (m, l) loads are issued together, and the next chunk's before this one is
+// summed, so even a pair cut into a hundred pieces costs about one memory round trip.
+// Across chunks the sums are rescaled to the running maximum.  Every sum runs in a fixed
+// order, so the result is deterministic.
+constexpr int kFixPieces = 32;
+
 template <int D, int G>
 __global__ void __launch_bounds__(64)
 decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_t num_kv_heads,
                     int32_t W, const float* __restrict__ ws_part, const float* __restrict__ ws_ml,
                     int32_t* __restrict__ ws_claim, uint16_t* __restrict__ out) {
-  constexpr int DPT = D / 64;
+  constexpr int C4 = D / 4;                  // 16-byte chunks of a partial row
+  constexpr int PG = 64 / C4;                // pieces per pass
+  constexpr int NP = kFixPieces / PG;        // passes per chunk
+  static_assert(C4 <= 64 && 64 % C4 == 0 && kFixPieces % PG == 0, "unsupported head_dim");
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int g = h / G;
   const int col = h % G;
-  if (h == 0 && b == 0 && threadIdx.x == 0) atomicExch(ws_claim, 0);   // for the next launch
+  const int lane = threadIdx.x;
+  if (h == 0 && b == 0 && lane == 0) atomicExch(ws_claim, 0);   // for the next launch
   const int64_t R = int64_t(num_kv_heads) * prefix[num_seqs];
   const int nr = prefix[b + 1] - prefix[b];
   if (nr == 0 || R == 0) return;
@@ -572,51 +589,73 @@ decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_
   const int64_t e = s + nr;                                               // past the last
   const int w0 = sp.piece(s), w1 = sp.piece(e - 1);
   if (w0 == w1) return;                      // finished in place
-  // Lane i handles pieces i, i+64, ...: their (m, l) loads are independent, and the
-  // partial rows are then summed in piece order with many loads in flight.
-  const int lane = threadIdx.x;
   const int np = w1 - w0 + 1;
   auto slot_of = [&](int w) {
     const int k = sp.start(w) >= s ? 0 : 1;
     return (w * 2 + k) * G + col;
   };
-  float M = -INFINITY;
-  for (int i = lane; i < np; i += 64) M = fmaxf(M, ws_ml[int64_t(slot_of(w0 + i)) * 2]);
+  const int c = lane % C4, pg = lane / C4;
+  float M = -INFINITY, den = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // Issue every load of the chunk at c0.  Lane i < kFixPieces locates piece c0 + i once
+  // (the split's divisions) and reads its (m, l); the row loads get slots by shuffles.
+  auto load = [&](int c0, f32x4_t (&row)[NP], float& my_m, float& my_l) {
+    const bool mine = lane < kFixPieces && c0 + lane < np;
+    const int my_slot = mine ? slot_of(w0 + c0 + lane) : 0;
+    my_m = mine ? ws_ml[int64_t(my_slot) * 2] : -INFINITY;
+    my_l = mine ? ws_ml[int64_t(my_slot) * 2 + 1] : 0.f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float den = 0.f, num[DPT];
-#pragma unroll
-  for (int j = 0; j < DPT; ++j) num[j] = 0.f;
-  for (int c0 = 0; c0 < np; c0 += 64) {
-    const int i = c0 + lane;
-    int my_slot = 0;
-    float wt = 0.f;
-    if (i < np) {
-      my_slot = slot_of(w0 + i);
-      wt = fast_exp2(ws_ml[int64_t(my_slot) * 2] - M);
-      den = fmaf(wt, ws_ml[int64_t(my_slot) * 2 + 1], den);
+    for (int k = 0; k < NP; ++k) {
+      const int src = k * PG + pg;
+      const int64_t sl = __shfl(my_slot, src);
+      row[k] = c0 + src < np ? *reinterpret_cast<const f32x4_t*>(ws_part + sl * D + 4 * c)
+                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const int n = np - c0 < 64 ? np - c0 : 64;
-    auto add = [&](int jp) {
-      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), jp));
-      const int64_t sj = __builtin_amdgcn_readlane(my_slot, jp);
+  };
+  // Fold a loaded chunk into the running sums (pieces past np have m = -inf, weight 0).
+  auto consume = [&](const f32x4_t (&row)[NP], float my_m, float my_l) {
+    float mn = my_m;
 #pragma unroll
-      for (int j = 0; j < DPT; ++j) num[j] = fmaf(wj, ws_part[sj * D + lane + 64 * j], num[j]);
-    };
-    int jp = 0;
-    for (; jp + 8 <= n; jp += 8) {
+    for (int off = 32; off >= 1; off >>= 1) mn = fmaxf(mn, __shfl_xor(mn, off));
+    mn = fmaxf(mn, M);
+    const float alpha = fast_exp2(M - mn);        // 0 on the first chunk (M = -inf)
+    acc *= alpha;
+    den *= alpha;
+    M = mn;
+    const float my_w = fast_exp2(my_m - M);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) add(jp + u);
+    for (int k = 0; k < NP; ++k) {
+      const int src = k * PG + pg;
+      const float wt = __shfl(my_w, src);
+      acc += wt * row[k];
+      den = fmaf(wt, __shfl(my_l, src), den);     // every lane of a piece group alike
     }
-    for (; jp < n; ++jp) add(jp);
+  };
+  // Two chunks in flight: the next chunk's loads go out before this one is folded in.
+  f32x4_t ra[NP], rb[NP];
+  float ma, la, mb, lb;
+  load(0, ra, ma, la);
+  for (int c0 = 0; c0 < np; c0 += 2 * kFixPieces) {
+    const bool has_b = c0 + kFixPieces < np;
+    if (has_b) load(c0 + kFixPieces, rb, mb, lb);
+    consume(ra, ma, la);
+    if (!has_b) break;
+    if (c0 + 2 * kFixPieces < np) load(c0 + 2 * kFixPieces, ra, ma, la);
+    consume(rb, mb, lb);
   }
+  // sum the PG piece groups (lanes c, c + C4, ...) in a fixed order
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-  const float inv = 1.0f / den;
-  const int64_t row = int64_t(b) * num_kv_heads * G + h;
+  for (int off = C4; off < 64; off <<= 1) {
 #pragma unroll
-  for (int j = 0; j < DPT; ++j)
-    out[row * D + threadIdx.x + 64 * j] = __builtin_bit_cast(uint16_t, (__bf16)(num[j] * inv));
+    for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], off);
+    den += __shfl_xor(den, off);
+  }
+  if (lane < C4) {
+    const float inv = 1.0f / den;
+    const int64_t orow = int64_t(b) * num_kv_heads * G + h;
+    const u32x2_t w2 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2_t*>(out + orow * D + 4 * lane) = w2;
+  }
 }
 
 // ---- fp32: VALU ---------------------------------------------------------------------------

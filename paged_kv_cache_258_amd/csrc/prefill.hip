@@ -328,6 +328,9 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     bf16x8_t kf[KS], vf[2][DT], pf[2];
     f32x16_t s[QB];
     read_k(st, kb, kf);
+    // all K fragment reads go out before the first MFMA, which then waits only for its
+    // own (left to itself the compiler reads one fragment, waits, multiplies, and so on)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
       if (k0h < diag + min(wq0 + qb * 32 + 32, lq)) qk(kf, qb, s[qb]);

@@ -221,3 +221,11 @@ def test_decode_tail_units_claimed_in_any_order(wgs, monkeypatch):
     for i in range(1, len(outs)):
         assert torch.equal(outs[i].view(torch.int16), outs[0].view(torch.int16)), \
             f"call {i} differs bitwise"
+
+
+def test_decode_long_pair_merged_over_several_chunks():
+    # One 40960-token sequence over the full grid: every (sequence, KV head) pair is cut
+    # into ~128 pieces, more than the fixup merges per memory round trip, so the merge
+    # runs over several chunks with the running-maximum rescale between them.
+    case = random_case(700, [40960], wl.QWEN3_8B)
+    check(case, "one 40960-token sequence")
