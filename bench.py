@@ -72,15 +72,6 @@ def stats_us(ms_list):
             "min_us": round(1e3 * xs[0], 2)}
 
 
-def hold_stream(ms):
-    """Keep the GPU busy for about `ms` with a spin kernel, so that the host enqueues the
-    timed calls while the GPU is still busy and a host-side hiccup cannot open gaps
-    inside the timed region."""
-    import torch
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
-
-
 def device_peaks(props):
     """Spec peaks beside the peaks implied by the device's own properties.
 
@@ -158,7 +149,6 @@ def bench_decode(dev, steps, warmup):
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    hold_stream(10.0)
     t0.record()
     for i in range(steps):
         step(i, evs[i])
@@ -212,7 +202,6 @@ def bench_prefill(dev, which, steps, warmup, settle_s=0.25):
 
     def timed(n):
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
-        hold_stream(10.0)
         for i in range(n):
             step(evs[i])
         torch.cuda.synchronize()
@@ -297,7 +286,6 @@ def bench_c5(dev, kind, reps, warmup):
         run_all()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    hold_stream(10.0)
     e0.record()
     for _ in range(reps):
         run_all()
