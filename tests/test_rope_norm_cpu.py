@@ -1,0 +1,135 @@
+"""Pins of the q/k RMSNorm + rotary + store oracle (oracle/rope_norm.py) against facts
+that do not come from the oracle itself: torch's own bf16 cast, closed forms of the
+rotary table, a hand-worked RMSNorm, the other rotary formulation the pages print (the
+rotate_half form), and invariants of the rotation.
+"""
+
+import numpy as np
+import torch
+
+from oracle import rope_norm as rn
+from oracle import ref
+
+BASE = 1.0e6     # Qwen3's rope theta
+
+
+def test_bf16_rounding_matches_torch_cast():
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32) * np.float32(3.0),
+        np.array([0.0, -0.0, 1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8),
+                  3.0e38, 1.0e-40, np.inf, -np.inf, 65504.0, 2.0 ** -126], dtype=np.float32),
+        (rng.standard_normal(2000) * 1e-38).astype(np.float32),     # subnormals
+    ]).astype(np.float32)
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(rn.f32_to_bf16_bits(vals), want)
+    # ties go to even: 1 + 2^-8 is halfway between 1 and 1 + 2^-7
+    assert rn.bf16_round(np.float32(1.0 + 2.0 ** -8)) == np.float32(1.0)
+    assert rn.bf16_round(np.float32(1.0 + 3 * 2.0 ** -8)) == np.float32(1.0 + 2.0 ** -6)
+    assert np.isnan(rn.bf16_round(np.float32(np.nan)))
+
+
+def test_rope_table_closed_forms():
+    d = 128
+    tab = rn.rope_cos_sin_table(2048, d, BASE)
+    assert tab.shape == (2048, d) and tab.dtype == np.float32
+    assert np.array_equal(tab[0], np.concatenate([np.ones(64), np.zeros(64)]).astype(np.float32))
+    assert np.allclose(tab[:, :64] ** 2 + tab[:, 64:] ** 2, 1.0, atol=1e-6)
+    t = np.arange(2048)
+    assert np.allclose(tab[:, 0], np.cos(t), atol=1e-6)      # frequency index 0 is 1 rad/pos
+    assert np.allclose(tab[:, 64], np.sin(t), atol=1e-6)
+    # frequency index 32 is base**(-64/128) = 1e-3 rad per position
+    assert abs(tab[1000, 32] - np.cos(1.0)) < 1e-6 and abs(tab[1000, 96] - np.sin(1.0)) < 1e-6
+    # the last frequency is base**(-126/128)
+    f = BASE ** (-126 / 128)
+    assert abs(tab[2047, 63] - np.cos(2047 * f)) < 1e-6
+
+
+def test_rms_norm_hand_worked_example():
+    # x = (3, 4): mean square 12.5, 1/sqrt(12.5) = 0.2828427; x * r = (0.848528, 1.131371)
+    # -> bf16 (0.84765625, 1.1328125); times w = (1, 2) -> (0.84765625, 2.265625)
+    out = rn.rms_norm_ref(np.array([[3.0, 4.0]], np.float32), np.array([1.0, 2.0], np.float32), 0.0)
+    assert np.array_equal(out, np.array([[0.84765625, 2.265625]], np.float32))
+
+
+def test_rms_norm_scale_invariance_and_unit_rms():
+    rng = np.random.default_rng(12)
+    x = rn.bf16_round(rng.standard_normal((64, 128)).astype(np.float32))
+    w = np.ones(128, np.float32)
+    a = rn.rms_norm_ref(x, w, 0.0)
+    b = rn.rms_norm_ref(x * np.float32(8.0), w, 0.0)      # exact power-of-two scaling
+    assert np.array_equal(a, b)
+    rms = np.sqrt(np.mean(a.astype(np.float64) ** 2, axis=-1))
+    assert np.all(np.abs(rms - 1.0) < 4e-3)                # bf16 rounding of each element
+    # eps matters only against the mean square: a zero row stays zero, no NaN
+    z = rn.rms_norm_ref(np.zeros((1, 128), np.float32), w, 1e-6)
+    assert np.array_equal(z, np.zeros((1, 128), np.float32))
+
+
+def test_rope_position_zero_is_identity_and_matches_rotate_half_form():
+    rng = np.random.default_rng(13)
+    d = 128
+    tab = rn.rope_cos_sin_table(4096, d, BASE)
+    x = rn.bf16_round(rng.standard_normal((300, 8, d)).astype(np.float32))
+    pos = rng.integers(0, 4096, size=300)
+    cos, sin = tab[pos][:, None, :64], tab[pos][:, None, 64:]
+    got = rn.apply_rope_ref(x, cos, sin)
+    # the transformers form: x * cat(cos, cos) + rotate_half(x) * cat(sin, sin), with
+    # rotate_half(x) = cat(-x2, x1) -- the same products and sums, so the same bits
+    cos2, sin2 = np.concatenate([cos, cos], -1), np.concatenate([sin, sin], -1)
+    rot_half = np.concatenate([-x[..., 64:], x[..., :64]], -1)
+    other = rn.bf16_round((x * cos2 + rot_half * sin2).astype(np.float32))
+    assert np.array_equal(got, other)
+    z = rn.apply_rope_ref(x, tab[0, None, None, :64], tab[0, None, None, 64:])
+    assert np.array_equal(z, x)
+
+
+def test_rope_preserves_pair_norms_and_depends_on_relative_position():
+    rng = np.random.default_rng(14)
+    d = 128
+    tab = rn.rope_cos_sin_table(8192, d, BASE)
+    q = rn.bf16_round(rng.standard_normal((50, d)).astype(np.float32))
+    k = rn.bf16_round(rng.standard_normal((50, d)).astype(np.float32))
+
+    def rot(x, p):
+        return rn.apply_rope_ref(x, tab[p][:, :64], tab[p][:, 64:]).astype(np.float64)
+
+    m = rng.integers(0, 4000, size=50)
+    n = rng.integers(0, 4000, size=50)
+    s = rng.integers(1, 4000, size=50)
+    a, b = rot(q, m), rot(k, n)
+    pair = lambda y: y[:, :64] ** 2 + y[:, 64:] ** 2
+    assert np.allclose(pair(a), pair(q.astype(np.float64)), rtol=2e-2, atol=1e-3)
+    d1 = np.sum(a * b, axis=1)
+    d2 = np.sum(rot(q, m + s) * rot(k, n + s), axis=1)
+    assert np.allclose(d1, d2, rtol=0, atol=0.15)           # bf16 outputs, |q||k| ~ 128
+    d3 = np.sum(rot(q, m + s) * rot(k, n), axis=1)          # a different offset changes it
+    assert np.mean(np.abs(d1 - d3)) > 1.0
+
+
+def test_composition_k_path_equals_q_path_and_store_semantics():
+    rng = np.random.default_rng(15)
+    t, h, d, nb, bs = 40, 2, 64, 8, 16
+    tab = rn.rope_cos_sin_table(1024, d, BASE)
+    qk = rng.standard_normal((t, h, d)).astype(np.float32)
+    v = rng.standard_normal((t, h, d)).astype(np.float32)
+    qkv = rn.f32_to_bf16_bits(np.concatenate([qk, qk, v], axis=1).reshape(t, -1))
+    w = rn.f32_to_bf16_bits(1.0 + 0.1 * rng.standard_normal(d).astype(np.float32))
+    pos = rng.integers(0, 1024, size=t)
+    slots = rng.permutation(nb * bs)[:t].astype(np.int32)
+    slots[::7] = -1
+    kp = np.full((nb, bs, h, d), 0x7FC0, np.uint16)          # NaN rows stay NaN unless stored
+    vp = kp.copy()
+    q_out, kp2, vp2 = rn.qk_norm_rope_store_ref(qkv, pos, w, w, tab, slots, kp, vp, h, h, 1e-6)
+    rows_k, rows_v = kp2.reshape(nb * bs, h, d), vp2.reshape(nb * bs, h, d)
+    vbits = qkv.reshape(t, 3 * h, d)[:, 2 * h:]
+    for i in range(t):
+        if slots[i] < 0:
+            continue
+        assert np.array_equal(rows_k[slots[i]], q_out[i])    # same data, same weights
+        assert np.array_equal(rows_v[slots[i]], vbits[i])    # v is stored untouched
+    untouched = np.setdiff1d(np.arange(nb * bs), slots[slots >= 0])
+    assert np.all(rows_k[untouched] == 0x7FC0) and np.all(rows_v[untouched] == 0x7FC0)
+    # the store part is the plain store
+    k_only, _ = ref.store_ref(q_out, vbits, kp, vp, slots)
+    assert np.array_equal(k_only, kp2)
