@@ -26,6 +26,8 @@ tens of milliseconds of back-to-back MFMA work run slower while the engine clock
 settles), and only then are the `steps` reported calls timed.
 peaks = the spec peaks beside CUs x max engine clock x 4096 flop/clock (bf16 MFMA) from the
 device properties.
+qk_norm_rope_store = the fused q/k RMSNorm + rotary + KV store over C3's 16384 prompt
+tokens and C2's 64 decode tokens: algorithmic bytes / mean event time vs 8 TB/s.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu] [--no-prefill] [--no-c5]
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -233,6 +235,58 @@ def bench_prefill(dev, which, steps, warmup, settle_s=0.25):
             "flop": flops, "prefill_call": pf_stats, "cold_prefill_call": cold,
             "settle_s": settle_s, "store_us": round(store_ms * 1e3, 2),
             "store_gbs": round(st_bytes / store_ms / 1e6, 1)}
+
+
+def bench_rope_store(dev, which, steps, warmup):
+    """q/k RMSNorm + rotary + KV store over the new tokens of a leg: the 16384 prompt tokens
+    of C3 (8 x 2048 at positions 0..2047) or the 64 decode tokens of C2 (at L_b - 1).
+    Synthetic inputs: N(0,1) projection output, weights of ones, a uniform [-1, 1] table
+    (its values do not change the work)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_258_amd as nkv
+    from paged_kv_cache_258_amd import accounting as acc
+    from paged_kv_cache_258_amd import workloads as wl
+
+    if which == "C3":
+        case = wl.c3_prefill(dev)
+        lens = np.diff(case.cu_seqlens_q)
+        pos = np.concatenate([np.arange(l) for l in lens]).astype(np.int32)
+    else:
+        case = wl.c2_decode(dev)
+        pos = (np.asarray(case.context_lens) - 1).astype(np.int32)
+    sh = case.shape
+    t = len(case.slot_mapping)
+    gen = torch.Generator(device=dev).manual_seed(wl.SEED_BASE + 77)
+    width = (sh.num_q_heads + 2 * sh.num_kv_heads) * sh.head_dim
+    qkv = wl.randn((t, width), gen, dev, "bf16")
+    w = torch.ones(sh.head_dim, dtype=torch.bfloat16, device=dev)
+    max_pos = 40960
+    table = torch.rand((max_pos, sh.head_dim), generator=gen, device=dev, dtype=torch.float32) * 2 - 1
+    pos_d, slots_d = i32(pos, dev), i32(case.slot_mapping, dev)
+    q_out = torch.empty((t, sh.num_q_heads, sh.head_dim), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        nkv.nkv_qk_norm_rope_store(qkv, pos_d, w, w, table, slots_d, case.k_cache, case.v_cache,
+                                   sh.num_q_heads, 1e-6, q_out=q_out)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    st = stats_us([a.elapsed_time(b) for a, b in evs])
+    nbytes = acc.qk_norm_rope_store_bytes(case.slot_mapping, sh.num_q_heads, sh.num_kv_heads,
+                                          sh.head_dim, sh.elem_bytes)
+    gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
+    log(f"[qk-norm+rope+store {which}] {t} tokens: {st['mean_us']:.1f} us -> {gbs:.0f} GB/s")
+    return {"workload": f"{which} tokens ({t})", "call": st, "bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def bench_c5(dev, kind, reps, warmup):
@@ -463,6 +517,10 @@ def main():
     if not args.no_prefill:
         prefill.append(bench_prefill(dev, "C3", args.steps, 2))
         prefill.append(bench_prefill(dev, "C4", args.steps, 2))
+    rope_store = []
+    if not args.no_prefill:
+        for which in ("C3", "C2"):
+            rope_store.append(bench_rope_store(dev, which, args.steps, 3))
     long_decode = []
     if not args.no_c5:
         for kind in ("a", "b"):
@@ -515,6 +573,7 @@ def main():
         "store": {"avg_launch_us": round(d["store_ms"] * 1e3, 2), "call": d["store_stats"],
                   "gbs": round(d["st_bytes"] / d["store_ms"] / 1e6, 1)},
         "prefill": prefill,
+        "qk_norm_rope_store": rope_store,
         "long_decode": long_decode,
         "cpu_baseline": cpu,
     }

@@ -11,6 +11,11 @@
  *                           cache_seqlens=context_lens, block_table, softmax_scale,
  *                           causal=True)
  *
+ * and the step right before the store in Qwen3Attention.forward (same page, §2), fused:
+ *
+ *   nkv_qk_norm_rope_store  q_norm(q), k_norm(k), rotary_emb(positions, q, k), then
+ *                           store_kvcache(k, v, ...)
+ *
  * Data layout (「同一个 Qwen3，两种写法」 §3.3, the pool allocated once at start-up):
  *   one layer's K pool and V pool are each a contiguous
  *   [num_blocks, block_size, num_kv_heads, head_dim] array, so a cache row ("slot")
@@ -36,7 +41,7 @@
  * store kernel: slots in [0, num_blocks*block_size) or -1 and unique within a call;
  * block ids in [0, num_blocks) for every logical block a sequence uses;
  * 1 <= context_lens[b] <= max_blocks_per_seq*block_size; cu_seqlens non-decreasing
- * with 0 <= Lq <= Lk per sequence.  A launch failure returns NKV_ERR_HIP.
+ * with 0 <= Lq <= Lk per sequence; positions in [0, max_position).  A launch failure returns NKV_ERR_HIP.
  * nkv_last_error() gives a human-readable reason for the last failure on the
  * calling thread.
  *
@@ -44,8 +49,8 @@
  * call first checks those device-resident preconditions on the device -- slots in
  * range and unique, the block ids each sequence uses in [0, num_blocks),
  * context_lens in [1, max_blocks_per_seq*block_size], cu_seqlens running sums from 0
- * with Lq <= Lk, Lq <= max_seqlen_q, Lk <= max_seqlen_k and cu_seqlens_q[B] = total_q
- * -- waits for the stream, and returns NKV_ERR_INVALID_ARG (naming the violation and
+ * with Lq <= Lk, Lq <= max_seqlen_q, Lk <= max_seqlen_k and cu_seqlens_q[B] = total_q,
+ * positions in [0, max_position) -- waits for the stream, and returns NKV_ERR_INVALID_ARG (naming the violation and
  * the first offending token or sequence) without launching the operation.  It
  * allocates nothing but synchronises the stream: a debugging aid, not for hot loops.
  */
@@ -107,6 +112,49 @@ nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_stride,
                                int32_t num_kv_heads, int32_t head_dim,
                                int32_t num_blocks, int32_t block_size,
                                nkv_dtype_t dtype, void* stream);
+
+/*
+ * Per-head RMSNorm of q and k, rotary embedding by position, and the KV store, in one
+ * pass over one layer's fused projection output (bf16 only).
+ * 「Nano-vLLM深度解读（下）」 §2 (Qwen3Attention.forward: q, k, v split from the
+ * projection; q_norm and k_norm over head_dim; rotary_emb(positions, q, k); attention,
+ * which stores k and v first, §4); 「同一个 Qwen3，两种写法」 §3.5 (rotation of the two
+ * halves by the cos/sin row of each position) and §3.6 (RMSNorm in float32).
+ * For token t and every head x of q (weight q_norm_weight) and of k (k_norm_weight):
+ *   n = bf16(x * rsqrt(mean(x*x) + eps)),  y = bf16(n * weight)     (float32 math)
+ *   (c, s) = cos_sin_cache[positions[t]] halves;  y1, y2 = halves of y
+ *   result = bf16(concat(y1*c - y2*s, y2*c + y1*s))
+ * The rotated q goes to q_out[t]; the rotated k and the untouched v go to row
+ * slot_mapping[t] of k_cache / v_cache (-1 skips the store, q_out is still written).
+ *
+ *   qkv            [num_tokens, (num_q_heads + 2*num_kv_heads) * head_dim] bf16: the q
+ *                  heads, then the k heads, then the v heads of a token; rows
+ *                  qkv_row_stride ELEMENTS apart (>= that width, a multiple of 4);
+ *                  8-byte aligned.
+ *   positions      [num_tokens] int32, each in [0, max_position).
+ *   q_norm_weight, k_norm_weight   [head_dim] bf16, 8-byte aligned.
+ *   cos_sin_cache  [max_position, head_dim] float32: head_dim/2 cosines, then the
+ *                  head_dim/2 sines; 16-byte aligned.  A model constant the caller
+ *                  builds once.
+ *   eps            RMSNorm epsilon in [0, 1] (Qwen3: 1e-6).
+ *   slot_mapping   [num_tokens] int32, as for nkv_store_kvcache.
+ *   q_out          [num_tokens, num_q_heads, head_dim] bf16 contiguous, 8-byte aligned;
+ *                  must not alias qkv.
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim] bf16, 8-byte
+ *                  aligned.
+ *   head_dim in {64, 128}; dtype must be NKV_BF16 (NKV_F32: NKV_ERR_UNSUPPORTED).
+ * Preconditions checked in checking mode: positions in range, slots as for the store.
+ * num_tokens == 0 is a no-op.
+ */
+nkv_status_t nkv_qk_norm_rope_store(const void* qkv, int64_t qkv_row_stride,
+                                    const int32_t* positions, const void* q_norm_weight,
+                                    const void* k_norm_weight, const float* cos_sin_cache,
+                                    int32_t max_position, float eps,
+                                    const int32_t* slot_mapping, int32_t num_tokens,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    void* q_out, void* k_cache, void* v_cache,
+                                    int32_t num_blocks, int32_t block_size, nkv_dtype_t dtype,
+                                    void* stream);
 
 /*
  * Causal varlen prefill attention over the paged pools.

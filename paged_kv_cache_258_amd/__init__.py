@@ -1,4 +1,5 @@
-"""nkv: the paged KV-cache data plane (store, paged prefill, paged decode) for MI355X.
+"""nkv: the paged KV-cache data plane (store, paged prefill, paged decode, and the fused
+q/k norm + rotary + store before them) for MI355X.
 
 The compute lives in ``libnkv.so`` (HIP kernels for gfx950 behind the C ABI of
 ``include/nkv.h``); this package is its thin Python binding plus the seeded input
@@ -12,6 +13,7 @@ from ._lib import (  # noqa: F401
     nkv_paged_attn_decode,
     nkv_paged_attn_decode_workspace_size,
     nkv_paged_attn_prefill,
+    nkv_qk_norm_rope_store,
     nkv_store_kvcache,
 )
 
@@ -19,6 +21,7 @@ __all__ = [
     "NkvError",
     "load",
     "nkv_store_kvcache",
+    "nkv_qk_norm_rope_store",
     "nkv_paged_attn_prefill",
     "nkv_paged_attn_decode",
     "nkv_paged_attn_decode_workspace_size",

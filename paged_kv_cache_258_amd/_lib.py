@@ -25,6 +25,7 @@ EXPORTS = (
     "nkv_status_string",
     "nkv_last_error",
     "nkv_store_kvcache",
+    "nkv_qk_norm_rope_store",
     "nkv_paged_attn_prefill",
     "nkv_paged_attn_decode_workspace_size",
     "nkv_paged_attn_decode",
@@ -61,6 +62,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nkv_store_kvcache.restype = ctypes.c_int
     lib.nkv_store_kvcache.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_p, c_p, c_i32,
                                       c_i32, c_i32, c_i32, c_i32, ctypes.c_int, c_p]
+    lib.nkv_qk_norm_rope_store.restype = ctypes.c_int
+    lib.nkv_qk_norm_rope_store.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_i32, c_f, c_p, c_i32,
+                                           c_i32, c_i32, c_i32, c_p, c_p, c_p, c_i32, c_i32,
+                                           ctypes.c_int, c_p]
     lib.nkv_paged_attn_prefill.restype = ctypes.c_int
     lib.nkv_paged_attn_prefill.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i32,
                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
@@ -134,6 +139,44 @@ def nkv_store_kvcache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
     _check(lib.nkv_store_kvcache(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
                                  _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), n, hkv, d,
                                  nb, bs, _dtype(key), _stream(key)), "nkv_store_kvcache")
+
+
+def nkv_qk_norm_rope_store(qkv: torch.Tensor, positions: torch.Tensor, q_norm_weight: torch.Tensor,
+                           k_norm_weight: torch.Tensor, cos_sin_cache: torch.Tensor,
+                           slot_mapping: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           num_q_heads: int, eps: float, q_out: torch.Tensor | None = None) -> torch.Tensor:
+    """q/k RMSNorm + rotary + KV store of one layer; returns the rotated q [T, Hq, D].
+
+    qkv: [T, (Hq + 2 Hkv) * D] bf16 (rows may be strided), positions / slot_mapping: [T]
+    int32, weights: [D] bf16, cos_sin_cache: [max_position, D] float32 (cos half, sin half).
+    """
+    lib = load()
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if qkv.dim() != 2 or qkv.stride(1) != 1:
+        raise ValueError("qkv must be [T, (Hq + 2 Hkv) * D] with contiguous rows")
+    t = qkv.shape[0]
+    if qkv.shape[1] != (num_q_heads + 2 * hkv) * d:
+        raise ValueError("qkv width is not (num_q_heads + 2 * num_kv_heads) * head_dim")
+    _int32_dev(positions, "positions")
+    _int32_dev(slot_mapping, "slot_mapping")
+    if positions.numel() != t or slot_mapping.numel() != t:
+        raise ValueError("positions and slot_mapping need one entry per token")
+    for w, name in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        if w.numel() != d or not w.is_contiguous() or w.dtype != qkv.dtype:
+            raise ValueError(f"{name} must be a contiguous [head_dim] tensor of qkv's dtype")
+    if (cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != d or not cos_sin_cache.is_contiguous()
+            or cos_sin_cache.dtype != torch.float32):
+        raise ValueError("cos_sin_cache must be a contiguous float32 [max_position, head_dim] tensor")
+    if q_out is None:
+        q_out = torch.empty((t, num_q_heads, d), dtype=qkv.dtype, device=qkv.device)
+    elif q_out.shape != (t, num_q_heads, d) or not q_out.is_contiguous() or q_out.dtype != qkv.dtype:
+        raise ValueError("q_out must be a contiguous [T, Hq, D] tensor of qkv's dtype")
+    _check(lib.nkv_qk_norm_rope_store(_ptr(qkv), qkv.stride(0), _ptr(positions), _ptr(q_norm_weight),
+                                      _ptr(k_norm_weight), _ptr(cos_sin_cache), cos_sin_cache.shape[0],
+                                      float(eps), _ptr(slot_mapping), t, num_q_heads, hkv, d,
+                                      _ptr(q_out), _ptr(k_cache), _ptr(v_cache), nb, bs, _dtype(qkv),
+                                      _stream(qkv)), "nkv_qk_norm_rope_store")
+    return q_out
 
 
 def nkv_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

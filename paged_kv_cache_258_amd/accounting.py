@@ -58,3 +58,17 @@ def prefill_min_bytes(cu_seqlens_q, cu_seqlens_k, num_q_heads: int, num_kv_heads
     tk = int(np.asarray(cu_seqlens_k)[-1])
     return (2 * tq * num_q_heads * head_dim * elem_bytes
             + 2 * tk * num_kv_heads * head_dim * elem_bytes)
+
+
+def qk_norm_rope_store_bytes(slot_mapping, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                             elem_bytes: int) -> int:
+    """Read every token's q, k, v heads, its position and slot and its cos/sin row (fp32),
+    the two norm weights once; write q back and k, v of the tokens that have a slot."""
+    slots = np.asarray(slot_mapping)
+    t = len(slots)
+    written = int((slots != -1).sum())
+    return (t * (num_q_heads + 2 * num_kv_heads) * head_dim * elem_bytes   # q, k, v in
+            + t * (4 + 4 + head_dim * 4)                                  # position, slot, table row
+            + 2 * head_dim * elem_bytes                                   # weights
+            + t * num_q_heads * head_dim * elem_bytes                     # q out
+            + written * 2 * num_kv_heads * head_dim * elem_bytes)         # k, v rows stored

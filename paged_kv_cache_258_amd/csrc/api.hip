@@ -126,6 +126,7 @@ const char* violation_name(int mask) {
   if (mask & nkv::kValidateSeqlens) return "cu_seqlens not running sums within max_seqlen / total_q";
   if (mask & nkv::kValidateBlockId) return "block_table id outside [0, num_blocks)";
   if (mask & nkv::kValidateContextLen) return "context_lens entry outside [1, max_blocks_per_seq*block_size]";
+  if (mask & nkv::kValidatePosition) return "positions entry outside [0, max_position)";
   return "unknown violation";
 }
 
@@ -190,6 +191,49 @@ NKV_EXPORT nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_strid
     if (vs != NKV_OK) return vs;
   }
   return hip_status(nkv::launch_store(a, static_cast<hipStream_t>(stream)), "store launch");
+}
+
+NKV_EXPORT nkv_status_t nkv_qk_norm_rope_store(
+    const void* qkv, int64_t qkv_row_stride, const int32_t* positions, const void* q_norm_weight,
+    const void* k_norm_weight, const float* cos_sin_cache, int32_t max_position, float eps,
+    const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, void* q_out, void* k_cache, void* v_cache, int32_t num_blocks,
+    int32_t block_size, nkv_dtype_t dtype, void* stream) {
+  if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  if (dtype != NKV_BF16) return fail(NKV_ERR_UNSUPPORTED, "q/k norm + rotary is implemented for bf16 only");
+  if (num_tokens < 0) return fail(NKV_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_q_heads <= 0 || num_kv_heads <= 0) return fail(NKV_ERR_INVALID_ARG, "head counts must be positive");
+  if (head_dim != 64 && head_dim != 128) return fail(NKV_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (num_blocks <= 0 || block_size <= 0) return fail(NKV_ERR_INVALID_ARG, "num_blocks and block_size must be positive");
+  if (int64_t(num_blocks) * block_size > int64_t(INT32_MAX))
+    return fail(NKV_ERR_UNSUPPORTED, "pool has more than 2^31-1 rows");
+  if (max_position <= 0) return fail(NKV_ERR_INVALID_ARG, "max_position must be positive");
+  if (!(eps >= 0.0f) || eps > 1.0f) return fail(NKV_ERR_INVALID_ARG, "eps must lie in [0, 1]");
+  const int64_t slots_per_token = int64_t(num_q_heads) + 2 * int64_t(num_kv_heads);
+  if (qkv_row_stride < slots_per_token * head_dim)
+    return fail(NKV_ERR_INVALID_ARG, "qkv row stride below (num_q_heads + 2*num_kv_heads)*head_dim");
+  if (qkv_row_stride % 4 != 0) return fail(NKV_ERR_INVALID_ARG, "qkv row stride must be a multiple of 4 elements");
+  if (num_tokens == 0) return ok();
+  if (!qkv || !positions || !q_norm_weight || !k_norm_weight || !cos_sin_cache || !slot_mapping ||
+      !q_out || !k_cache || !v_cache)
+    return fail(NKV_ERR_INVALID_ARG, "null pointer argument");
+  auto aligned8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7) == 0; };
+  if (!aligned8(qkv) || !aligned8(q_norm_weight) || !aligned8(k_norm_weight) || !aligned8(q_out) ||
+      !aligned8(k_cache) || !aligned8(v_cache) || !aligned16(cos_sin_cache))
+    return fail(NKV_ERR_INVALID_ARG, "qkv/weights/q_out/caches need 8-byte and cos_sin_cache 16-byte alignment");
+  nkv::RopeStoreArgs a{qkv, qkv_row_stride, positions, q_norm_weight, k_norm_weight, cos_sin_cache, eps,
+                       slot_mapping, num_tokens, num_q_heads, num_kv_heads, head_dim, q_out, k_cache,
+                       v_cache, num_cus()};
+  if (validating()) {
+    nkv::ValidateResult r{};
+    const hipError_t e = nkv::validate_rope_store(positions, slot_mapping, num_tokens, max_position,
+                                                  int64_t(num_blocks) * block_size,
+                                                  static_cast<hipStream_t>(stream), &r);
+    const nkv_status_t vs = checked(e, r, "nkv_qk_norm_rope_store");
+    if (vs != NKV_OK) return vs;
+  }
+  return hip_status(nkv::launch_qk_norm_rope_store(a, static_cast<hipStream_t>(stream)),
+                    "q/k norm + rotary + store launch");
 }
 
 NKV_EXPORT nkv_status_t nkv_paged_attn_prefill(

@@ -24,6 +24,27 @@ struct StoreArgs {
   int num_cus;
 };
 
+// q/k RMSNorm + rotary + store (bf16).  Strides in elements.
+struct RopeStoreArgs {
+  const void* qkv;
+  int64_t qkv_row;
+  const int32_t* positions;
+  const void* q_weight;
+  const void* k_weight;
+  const float* cos_sin;
+  float eps;
+  const int32_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+  int num_cus;
+};
+hipError_t launch_qk_norm_rope_store(const RopeStoreArgs& a, hipStream_t st);
+
 struct PagedArgs {
   const void* k_cache;
   const void* v_cache;
@@ -85,6 +106,7 @@ enum : int {
   kValidateSeqlens = 4,         // cu_seqlens not running sums / lengths out of bounds
   kValidateBlockId = 8,         // a used block_table entry outside [0, num_blocks)
   kValidateContextLen = 16,     // context_lens[b] outside [1, max_blocks_per_seq*block_size]
+  kValidatePosition = 32,       // positions[t] outside [0, max_position)
 };
 struct ValidateResult {
   int mask;
@@ -96,6 +118,9 @@ hipError_t validate_prefill(const PrefillArgs& a, int32_t total_q, int32_t num_b
                             hipStream_t st, ValidateResult* r);
 hipError_t validate_decode(const DecodeArgs& a, int32_t num_blocks, hipStream_t st,
                            ValidateResult* r);
+
+hipError_t validate_rope_store(const int32_t* positions, const int32_t* slots, int32_t n,
+                              int32_t max_position, int64_t rows, hipStream_t st, ValidateResult* r);
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

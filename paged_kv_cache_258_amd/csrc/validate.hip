@@ -12,7 +12,9 @@
 //                 non-decreasing, cu_q[B] = total_q, per sequence 0 <= Lq <= Lk,
 //                 Lq <= max_seqlen_q, Lk <= max_seqlen_k;
 //   context_lens  1 <= L <= max_blocks_per_seq*block_size (the decode query attends to
-//                 the token stored just before the call).
+//                 the token stored just before the call);
+//   positions     rows of the cos/sin table, [0, max_position) (「同一个 Qwen3，两种写法」
+//                 §3.5, the table is indexed by position).
 // A violation sets one bit of a mask and lowers the first offending index.  The host
 // copies both back after the stream has drained and returns NKV_ERR_INVALID_ARG, so
 // invalid arrays never reach the store or attention kernels.  The flags live in a
@@ -107,6 +109,12 @@ validate_decode_kernel(const int32_t* __restrict__ context_lens,
   check_blocks(block_table + int64_t(b) * max_blocks, len, log2_bs, num_blocks, b);
 }
 
+__global__ void __launch_bounds__(256)
+validate_positions_kernel(const int32_t* __restrict__ positions, int32_t n, int32_t max_position) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n && (positions[i] < 0 || positions[i] >= max_position)) report(kValidatePosition, i);
+}
+
 namespace {
 
 // Drain the checks and read the flags back (the stream is synchronised here).
@@ -132,6 +140,17 @@ hipError_t validate_store(const int32_t* slots, int32_t n, int64_t rows, hipStre
   if (n > 0)
     hipLaunchKernelGGL(validate_slots_kernel, dim3((n + 255) / 256), dim3(256), 0, st, slots, n,
                        rows);
+  return collect(st, r);
+}
+
+hipError_t validate_rope_store(const int32_t* positions, const int32_t* slots, int32_t n,
+                              int32_t max_position, int64_t rows, hipStream_t st, ValidateResult* r) {
+  hipLaunchKernelGGL(validate_reset_kernel, dim3(1), dim3(64), 0, st);
+  if (n > 0) {
+    hipLaunchKernelGGL(validate_positions_kernel, dim3((n + 255) / 256), dim3(256), 0, st, positions, n,
+                       max_position);
+    hipLaunchKernelGGL(validate_slots_kernel, dim3((n + 255) / 256), dim3(256), 0, st, slots, n, rows);
+  }
   return collect(st, r);
 }
 

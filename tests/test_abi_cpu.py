@@ -151,3 +151,40 @@ def test_prefill_rejects(lib, kw, status):
 def test_prefill_empty_is_noop(lib):
     assert prefill(lib, tq=0, mq=0, q=None, out=None) == _lib.NKV_OK
     assert prefill(lib, b=0, table=FAKE) == _lib.NKV_OK
+
+
+def rope_store(lib, **kw):
+    a = dict(qkv=FAKE, rs=6144, pos=FAKE, wq=FAKE, wk=FAKE, cs=FAKE, maxpos=40960, eps=1e-6,
+             slots=FAKE, n=64, hq=32, hkv=8, d=128, qout=FAKE, kc=FAKE, vc=FAKE, nb=600, bs=256,
+             dtype=1, stream=None)
+    a.update(kw)
+    return lib.nkv_qk_norm_rope_store(a["qkv"], a["rs"], a["pos"], a["wq"], a["wk"], a["cs"],
+                                      a["maxpos"], a["eps"], a["slots"], a["n"], a["hq"],
+                                      a["hkv"], a["d"], a["qout"], a["kc"], a["vc"], a["nb"],
+                                      a["bs"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), _lib.NKV_ERR_UNSUPPORTED),          # fp32: bf16 only
+    (dict(dtype=5), _lib.NKV_ERR_INVALID_ARG),
+    (dict(d=96), _lib.NKV_ERR_UNSUPPORTED),
+    (dict(rs=6000), _lib.NKV_ERR_INVALID_ARG),          # below (Hq + 2 Hkv) * D
+    (dict(rs=6146), _lib.NKV_ERR_INVALID_ARG),          # not a multiple of 4 elements
+    (dict(maxpos=0), _lib.NKV_ERR_INVALID_ARG),
+    (dict(eps=-1.0), _lib.NKV_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), _lib.NKV_ERR_INVALID_ARG),
+    (dict(hkv=0), _lib.NKV_ERR_INVALID_ARG),
+    (dict(n=-3), _lib.NKV_ERR_INVALID_ARG),
+    (dict(pos=None), _lib.NKV_ERR_INVALID_ARG),
+    (dict(qout=None), _lib.NKV_ERR_INVALID_ARG),
+    (dict(cs=FAKE + 8), _lib.NKV_ERR_INVALID_ARG),     # table needs 16-byte alignment
+    (dict(qkv=FAKE + 4), _lib.NKV_ERR_INVALID_ARG),    # 8-byte alignment
+    (dict(nb=1 << 24, bs=1 << 10), _lib.NKV_ERR_UNSUPPORTED),
+])
+def test_rope_store_rejects(lib, kw, status):
+    assert rope_store(lib, **kw) == status
+    assert lib.nkv_last_error() != b""
+
+
+def test_rope_store_zero_tokens_is_noop(lib):
+    assert rope_store(lib, n=0, qkv=None, pos=None, slots=None, qout=None, kc=None, vc=None) == _lib.NKV_OK

@@ -146,3 +146,31 @@ def test_prefill_rejects_bad_indices(checking, kind):
                                                   pre.shape.scale, out=out),
                    f"prefill {kind}")
     assert bool((out == 7.0).all()), "prefill output written despite invalid indices"
+
+
+@pytest.mark.parametrize("kind", ["position_high", "position_negative", "slot_duplicate"])
+def test_rope_store_rejects_bad_indices(checking, kind):
+    from paged_kv_cache_258_amd import nkv_qk_norm_rope_store
+    dev = require_gpu()
+    t, hq, hkv, d, nb, bs = 40, 8, 2, 128, 8, 16
+    gen = torch.Generator(device=dev).manual_seed(33)
+    qkv = wl.randn((t, (hq + 2 * hkv) * d), gen, dev, "bf16")
+    w = torch.ones(d, dtype=torch.bfloat16, device=dev)
+    table = torch.zeros((100, d), dtype=torch.float32, device=dev)
+    pos = np.arange(t, dtype=np.int32)
+    slots = np.arange(t, dtype=np.int32)
+    if kind == "position_high":
+        pos[3] = 100
+    elif kind == "position_negative":
+        pos[9] = -1
+    else:
+        slots[11] = slots[2]
+    kc = wl.nan_pool(nb, bs, hkv, d, "bf16", dev)
+    vc = wl.nan_pool(nb, bs, hkv, d, "bf16", dev)
+    before = raw_bytes(kc)
+    q_out = torch.full((t, hq, d), 7.0, dtype=torch.bfloat16, device=dev)
+    expect_invalid(lambda: nkv_qk_norm_rope_store(qkv, dev_i32(pos, dev), w, w, table,
+                                                  dev_i32(slots, dev), kc, vc, hq, 1e-6, q_out=q_out),
+                   f"rope_store {kind}")
+    assert bool((q_out == 7.0).all()), "q_out written despite invalid indices"
+    assert np.array_equal(raw_bytes(kc), before), "pool written despite invalid indices"
