@@ -129,18 +129,18 @@ nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_stride,
  *
  *   qkv            [num_tokens, (num_q_heads + 2*num_kv_heads) * head_dim] bf16: the q
  *                  heads, then the k heads, then the v heads of a token; rows
- *                  qkv_row_stride ELEMENTS apart (>= that width, a multiple of 4);
- *                  8-byte aligned.
+ *                  qkv_row_stride ELEMENTS apart (>= that width, a multiple of 8);
+ *                  16-byte aligned.
  *   positions      [num_tokens] int32, each in [0, max_position).
- *   q_norm_weight, k_norm_weight   [head_dim] bf16, 8-byte aligned.
+ *   q_norm_weight, k_norm_weight   [head_dim] bf16, 16-byte aligned.
  *   cos_sin_cache  [max_position, head_dim] float32: head_dim/2 cosines, then the
  *                  head_dim/2 sines; 16-byte aligned.  A model constant the caller
  *                  builds once.
  *   eps            RMSNorm epsilon in [0, 1] (Qwen3: 1e-6).
  *   slot_mapping   [num_tokens] int32, as for nkv_store_kvcache.
- *   q_out          [num_tokens, num_q_heads, head_dim] bf16 contiguous, 8-byte aligned;
+ *   q_out          [num_tokens, num_q_heads, head_dim] bf16 contiguous, 16-byte aligned;
  *                  must not alias qkv.
- *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim] bf16, 8-byte
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim] bf16, 16-byte
  *                  aligned.
  *   head_dim in {64, 128}; dtype must be NKV_BF16 (NKV_F32: NKV_ERR_UNSUPPORTED).
  * Preconditions checked in checking mode: positions in range, slots as for the store.

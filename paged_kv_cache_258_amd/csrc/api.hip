@@ -212,15 +212,14 @@ NKV_EXPORT nkv_status_t nkv_qk_norm_rope_store(
   const int64_t slots_per_token = int64_t(num_q_heads) + 2 * int64_t(num_kv_heads);
   if (qkv_row_stride < slots_per_token * head_dim)
     return fail(NKV_ERR_INVALID_ARG, "qkv row stride below (num_q_heads + 2*num_kv_heads)*head_dim");
-  if (qkv_row_stride % 4 != 0) return fail(NKV_ERR_INVALID_ARG, "qkv row stride must be a multiple of 4 elements");
+  if (qkv_row_stride % 8 != 0) return fail(NKV_ERR_INVALID_ARG, "qkv row stride must be a multiple of 8 elements");
   if (num_tokens == 0) return ok();
   if (!qkv || !positions || !q_norm_weight || !k_norm_weight || !cos_sin_cache || !slot_mapping ||
       !q_out || !k_cache || !v_cache)
     return fail(NKV_ERR_INVALID_ARG, "null pointer argument");
-  auto aligned8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7) == 0; };
-  if (!aligned8(qkv) || !aligned8(q_norm_weight) || !aligned8(k_norm_weight) || !aligned8(q_out) ||
-      !aligned8(k_cache) || !aligned8(v_cache) || !aligned16(cos_sin_cache))
-    return fail(NKV_ERR_INVALID_ARG, "qkv/weights/q_out/caches need 8-byte and cos_sin_cache 16-byte alignment");
+  if (!aligned16(qkv) || !aligned16(q_norm_weight) || !aligned16(k_norm_weight) || !aligned16(q_out) ||
+      !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(cos_sin_cache))
+    return fail(NKV_ERR_INVALID_ARG, "qkv, weights, q_out, caches and cos_sin_cache need 16-byte alignment");
   nkv::RopeStoreArgs a{qkv, qkv_row_stride, positions, q_norm_weight, k_norm_weight, cos_sin_cache, eps,
                        slot_mapping, num_tokens, num_q_heads, num_kv_heads, head_dim, q_out, k_cache,
                        v_cache, num_cus()};

@@ -13,25 +13,44 @@
 //
 // Layout of the work: one wave per token (grid-stride over tokens), so the position, the
 // slot, the cos/sin row and the norm weights are read once per token and every head's
-// loads go out together.  A head of D dims is handled by D/8 lanes: lane j of a head holds
-// dims [4j, 4j+4) of the first half and the same dims of the second half, so the rotation
-// pairs live in one lane, and a head's mean square is a butterfly over its D/8 lanes.  The
-// 64/(D/8) lane groups of a wave take head slots g, g + 64/(D/8), ... (q heads, then k,
-// then v, as the projection lays them out), up to 64 slots per pass.  Float contraction
-// is off so that the rotation rounds its two products and their sum separately, as the
-// listing's float32 tensor arithmetic does.  The head sums run over DPP lane moves in an
-// order that gives every lane of a head the same bits, and the reciprocal root is the
-// hardware's v_rsq_f32 (within an ulp, like the listing's rsqrt).
+// loads go out together.  A head of D dims is handled by D/8 lanes, lane j holding the
+// 8 consecutive dims [8j, 8j+8) as one 16-byte access.  The rotation pairs dim i with
+// dim i + D/2, which the lane D/16 positions away holds: after normalising, each lane
+// swaps its four packed bf16 words with that partner (a DPP row rotation by 8 for D = 128)
+// and computes the half of the rotation that lands in its own dims.  A head's mean
+// square is a sum over its D/8 lanes, in an order that gives every lane the same bits.
+// The 64/(D/8) lane groups of a wave take head slots g, g + 64/(D/8), ... (q heads, then
+// k, then v, as the projection lays them out), up to 64 slots per pass.  Float
+// contraction is off so that the rotation rounds its two products and their sum
+// separately, as the listing's float32 tensor arithmetic does; the reciprocal root is
+// the hardware's v_rsq_f32 (within an ulp, like the listing's rsqrt).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace nkv {
 
+#ifndef NKV_ROPE_WGS_PER_CU
+#define NKV_ROPE_WGS_PER_CU 16
+#endif
 constexpr int kRopeThreads = 256;
 constexpr int kRopeWaves = kRopeThreads / kWave;
 
-__device__ __forceinline__ float round_bf16(float x) {   // round to nearest even, to bf16
-  return __builtin_bit_cast(float, uint32_t(__builtin_bit_cast(uint16_t, (__bf16)x)) << 16);
+// the bf16 values of a packed pair, as floats
+__device__ __forceinline__ void unpack8(const u32x4_t& w, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+// the partner's word: lane j of a D/8-lane head group <- lane j ^ (D/16)
+template <int LPH>
+__device__ __forceinline__ uint32_t partner(uint32_t v) {
+  if constexpr (LPH == 16)
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kDppRowRor8, 0xf, 0xf, true));
+  else
+    return uint32_t(__shfl_xor(int(v), LPH / 2));
 }
 
 template <int D>
@@ -49,84 +68,85 @@ qk_norm_rope_store_kernel(const uint16_t* __restrict__ qkv, int64_t qkv_row,
   constexpr int GL = kWave / LPH;        // heads side by side in a wave
   constexpr int KR = kWave / GL;         // head rows per pass: GL * KR = 64 slots
   constexpr int H2 = D / 2;
+  static_assert(LPH == 8 || LPH == 16, "head_dim 64 or 128");
   const int lane = threadIdx.x % kWave;
   const int j = lane % LPH;
   const int g = lane / LPH;
+  const bool second = j >= LPH / 2;      // this lane's dims are in the second half
+  const int fi = 8 * j - (second ? H2 : 0);   // frequency index of its first dim
   const int nslots = num_q_heads + 2 * num_kv_heads;
   const int first_v = num_q_heads + num_kv_heads;
   const int64_t row_kv = int64_t(num_kv_heads) * D;   // pool row, elements
-  // per-lane constants: the norm weights of this lane's dims
-  const u32x2_t qa = *reinterpret_cast<const u32x2_t*>(q_weight + 4 * j);
-  const u32x2_t qb = *reinterpret_cast<const u32x2_t*>(q_weight + H2 + 4 * j);
-  const u32x2_t ka = *reinterpret_cast<const u32x2_t*>(k_weight + 4 * j);
-  const u32x2_t kb = *reinterpret_cast<const u32x2_t*>(k_weight + H2 + 4 * j);
-  const float wq1[4] = {bf16_lo(qa[0]), bf16_hi(qa[0]), bf16_lo(qa[1]), bf16_hi(qa[1])};
-  const float wq2[4] = {bf16_lo(qb[0]), bf16_hi(qb[0]), bf16_lo(qb[1]), bf16_hi(qb[1])};
-  const float wk1[4] = {bf16_lo(ka[0]), bf16_hi(ka[0]), bf16_lo(ka[1]), bf16_hi(ka[1])};
-  const float wk2[4] = {bf16_lo(kb[0]), bf16_hi(kb[0]), bf16_lo(kb[1]), bf16_hi(kb[1])};
+  float wq[8], wk[8];                    // the norm weights of this lane's dims
+  unpack8(*reinterpret_cast<const u32x4_t*>(q_weight + 8 * j), wq);
+  unpack8(*reinterpret_cast<const u32x4_t*>(k_weight + 8 * j), wk);
 
   for (int t = blockIdx.x * kRopeWaves + threadIdx.x / kWave; t < num_tokens;
        t += gridDim.x * kRopeWaves) {
     const int pos = __builtin_amdgcn_readfirstlane(positions[t]);
     const int32_t slot = __builtin_amdgcn_readfirstlane(slot_mapping[t]);
-    const f32x4_t c = *reinterpret_cast<const f32x4_t*>(cos_sin + int64_t(pos) * D + 4 * j);
-    const f32x4_t sn = *reinterpret_cast<const f32x4_t*>(cos_sin + int64_t(pos) * D + H2 + 4 * j);
+    const float* row = cos_sin + int64_t(pos) * D;
+    const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(row + fi);
+    const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(row + fi + 4);
+    const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(row + H2 + fi);
+    const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(row + H2 + fi + 4);
+    const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     const uint16_t* src = qkv + int64_t(t) * qkv_row;
-    for (int s0 = 0; s0 < nslots; s0 += GL * KR) {
-      u32x2_t a[KR], b[KR];
+    for (int sb = 0; sb < nslots; sb += GL * KR) {
+      u32x4_t a[KR];
 #pragma unroll
       for (int k = 0; k < KR; ++k) {                      // every load of the pass first
-        const int s = s0 + k * GL + g;
-        if (s < nslots) {
-          a[k] = *reinterpret_cast<const u32x2_t*>(src + int64_t(s) * D + 4 * j);
-          b[k] = *reinterpret_cast<const u32x2_t*>(src + int64_t(s) * D + H2 + 4 * j);
-        } else {
-          a[k] = u32x2_t{0, 0};
-          b[k] = u32x2_t{0, 0};
-        }
+        const int s = sb + k * GL + g;
+        a[k] = s < nslots ? *reinterpret_cast<const u32x4_t*>(src + int64_t(s) * D + 8 * j)
+                          : u32x4_t{0, 0, 0, 0};
       }
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
-        const int s = s0 + k * GL + g;
-        if (s0 + k * GL >= nslots) break;                // no group of this row has a slot
-        if (s >= first_v) {                              // v: stored as it is
-          if (s < nslots && slot >= 0) {
-            uint16_t* dst = v_cache + int64_t(slot) * row_kv + int64_t(s - first_v) * D;
-            *reinterpret_cast<u32x2_t*>(dst + 4 * j) = a[k];
-            *reinterpret_cast<u32x2_t*>(dst + H2 + 4 * j) = b[k];
-          }
+        const int s = sb + k * GL + g;
+        if (sb + k * GL >= nslots) break;                 // no group of this row has a slot
+        if (s >= first_v) {                               // v: stored as it is
+          if (s < nslots && slot >= 0)
+            *reinterpret_cast<u32x4_t*>(v_cache + int64_t(slot) * row_kv +
+                                        int64_t(s - first_v) * D + 8 * j) = a[k];
           continue;
         }
-        // q or k head: mean square over the head (8 squares here, a butterfly over its
-        // LPH lanes), then norm, cast, weight, cast, rotation, cast
+        // q or k head: mean square, norm, cast, weight, cast; swap with the partner;
+        // this lane's half of the rotation, cast
         const bool is_q = s < num_q_heads;
-        const float x1[4] = {bf16_lo(a[k][0]), bf16_hi(a[k][0]), bf16_lo(a[k][1]), bf16_hi(a[k][1])};
-        const float x2[4] = {bf16_lo(b[k][0]), bf16_hi(b[k][0]), bf16_lo(b[k][1]), bf16_hi(b[k][1])};
+        float x[8];
+        unpack8(a[k], x);
         float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ss += x1[i] * x1[i] + x2[i] * x2[i];
-        ss = group8_sum(ss);                             // DPP: every lane of the group
-        if constexpr (LPH == 16) ss += dpp<kDppRowRor8>(ss);   // gets the same sum
-        const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);   // v_rsq_f32
-        float o1[4], o2[4];
+        for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+        ss = group8_sum(ss);
+        if constexpr (LPH == 16) ss += dpp<kDppRowRor8>(ss);
+        const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+        u32x4_t yw;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float y1 = round_bf16(round_bf16(x1[i] * r) * (is_q ? wq1[i] : wk1[i]));
-          const float y2 = round_bf16(round_bf16(x2[i] * r) * (is_q ? wq2[i] : wk2[i]));
-          o1[i] = y1 * c[i] - y2 * sn[i];
-          o2[i] = y2 * c[i] + y1 * sn[i];
+          const float n0 = bf16_lo(pack_bf16x2(x[2 * i] * r, x[2 * i + 1] * r));
+          const float n1 = bf16_hi(pack_bf16x2(x[2 * i] * r, x[2 * i + 1] * r));
+          yw[i] = pack_bf16x2(n0 * (is_q ? wq[2 * i] : wk[2 * i]),
+                              n1 * (is_q ? wq[2 * i + 1] : wk[2 * i + 1]));
         }
-        const u32x2_t p1 = {pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
-        const u32x2_t p2 = {pack_bf16x2(o2[0], o2[1]), pack_bf16x2(o2[2], o2[3])};
+        u32x4_t pw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pw[i] = partner<LPH>(yw[i]);
+        float y[8], yp[8], o[8];
+        unpack8(yw, y);
+        unpack8(pw, yp);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)   // first half: y1 c - y2 s; second half: y2 c + y1 s
+          o[i] = second ? y[i] * c[i] + yp[i] * sn[i] : y[i] * c[i] - yp[i] * sn[i];
+        const u32x4_t ow = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                            pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
         uint16_t* dst = nullptr;
         if (is_q)
           dst = q_out + (int64_t(t) * num_q_heads + s) * D;
         else if (slot >= 0)
           dst = k_cache + int64_t(slot) * row_kv + int64_t(s - num_q_heads) * D;
-        if (dst) {
-          *reinterpret_cast<u32x2_t*>(dst + 4 * j) = p1;
-          *reinterpret_cast<u32x2_t*>(dst + H2 + 4 * j) = p2;
-        }
+        if (dst) *reinterpret_cast<u32x4_t*>(dst + 8 * j) = ow;
       }
     }
   }
@@ -135,7 +155,7 @@ qk_norm_rope_store_kernel(const uint16_t* __restrict__ qkv, int64_t qkv_row,
 hipError_t launch_qk_norm_rope_store(const RopeStoreArgs& a, hipStream_t st) {
   if (a.num_tokens == 0) return hipSuccess;
   int64_t blocks = (int64_t(a.num_tokens) + kRopeWaves - 1) / kRopeWaves;   // a wave per token
-  const int64_t cap = int64_t(a.num_cus) * 8;   // beyond that, waves walk more tokens
+  const int64_t cap = int64_t(a.num_cus) * NKV_ROPE_WGS_PER_CU;   // beyond, waves walk more tokens
   if (blocks > cap) blocks = cap;
   const auto* qkv = static_cast<const uint16_t*>(a.qkv);
   auto* q_out = static_cast<uint16_t*>(a.q_out);

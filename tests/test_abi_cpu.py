@@ -169,7 +169,7 @@ def rope_store(lib, **kw):
     (dict(dtype=5), _lib.NKV_ERR_INVALID_ARG),
     (dict(d=96), _lib.NKV_ERR_UNSUPPORTED),
     (dict(rs=6000), _lib.NKV_ERR_INVALID_ARG),          # below (Hq + 2 Hkv) * D
-    (dict(rs=6146), _lib.NKV_ERR_INVALID_ARG),          # not a multiple of 4 elements
+    (dict(rs=6148), _lib.NKV_ERR_INVALID_ARG),          # not a multiple of 8 elements
     (dict(maxpos=0), _lib.NKV_ERR_INVALID_ARG),
     (dict(eps=-1.0), _lib.NKV_ERR_INVALID_ARG),
     (dict(eps=float("nan")), _lib.NKV_ERR_INVALID_ARG),
@@ -178,7 +178,8 @@ def rope_store(lib, **kw):
     (dict(pos=None), _lib.NKV_ERR_INVALID_ARG),
     (dict(qout=None), _lib.NKV_ERR_INVALID_ARG),
     (dict(cs=FAKE + 8), _lib.NKV_ERR_INVALID_ARG),     # table needs 16-byte alignment
-    (dict(qkv=FAKE + 4), _lib.NKV_ERR_INVALID_ARG),    # 8-byte alignment
+    (dict(qkv=FAKE + 8), _lib.NKV_ERR_INVALID_ARG),    # 16-byte alignment
+    (dict(wq=FAKE + 8), _lib.NKV_ERR_INVALID_ARG),
     (dict(nb=1 << 24, bs=1 << 10), _lib.NKV_ERR_UNSUPPORTED),
 ])
 def test_rope_store_rejects(lib, kw, status):
