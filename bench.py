@@ -19,7 +19,8 @@ traffic = HBM bytes per decode call measured by rocprofv3 counters (FETCH_SIZE a
 WRITE_SIZE, calibrated on a plain copy of known size), read from
 profiles/decode_c2_counters.json when it was taken on the current decode sources.
 cpu_baseline = the float64 CPU oracle (store_ref + decode_ref) on the same C2 batch.
-decode_call / prefill_call = mean, median and minimum of the per-call event times.
+decode_call / prefill_call = mean, median and minimum of the per-call event times; the
+prefill legs' headline time is the median call.
 Prefill legs are timed in steady state: after the warm-up calls, 10 calls are timed at once
 (cold_prefill_call), the matrix cores are then kept busy for settle_s seconds (the first
 tens of milliseconds of back-to-back MFMA work run slower while the engine clock
@@ -223,8 +224,11 @@ def bench_prefill(dev, which, steps, warmup, settle_s=0.25):
         torch.cuda.synchronize()
     evs = timed(steps)
     store_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    pf_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     pf_stats = stats_us([e[1].elapsed_time(e[2]) for e in evs])
+    # The median call: a rare stall of tens of milliseconds inside one timed interval (seen
+    # on some boxes, in either leg) would otherwise dominate the mean of 50 sub-ms calls;
+    # the mean stays in prefill_call.
+    pf_ms = pf_stats["median_us"] * 1e-3
     flops = acc.prefill_flops(case.cu_seqlens_q, case.cu_seqlens_k, sh.num_q_heads, sh.head_dim)
     st_bytes = acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
     tflops = flops / pf_ms / 1e9
