@@ -23,6 +23,12 @@ What is computed, and where the pages define it:
   ``(x1*cos - x2*sin, x2*cos + x1*sin)`` cast back to the input dtype.
 * ``qk_norm_rope_store_ref`` -- the composition, with the store of the rotated k and the
   untouched v through ``slot_mapping`` as in ``ref.store_ref``.
+* ``add_rms_norm_ref`` -- the fused residual add + RMSNorm between decoder blocks,
+  「同一个 Qwen3，两种写法」 §3.6 (``add_rms_forward``): hidden state and residual are added in
+  float32, that sum cast to bf16 becomes the new residual, and the float32 sum (not its
+  bf16 copy) is normalised, cast to bf16 and multiplied by the weight.  Without a
+  residual (the first block) it is the plain RMSNorm of the hidden state and the hidden
+  state itself is the residual.
 
 Precision.  The listings fix it: norm and rotation run in float32 with a cast back to
 bf16 after the normalisation, after the weight product and after the rotation.  This
@@ -51,6 +57,7 @@ __all__ = [
     "rms_norm_ref",
     "apply_rope_ref",
     "qk_norm_rope_store_ref",
+    "add_rms_norm_ref",
 ]
 
 
@@ -123,3 +130,24 @@ def qk_norm_rope_store_ref(qkv_bits: np.ndarray, positions: np.ndarray, q_weight
     k_new, v_new = store_ref(f32_to_bf16_bits(k_rot), np.ascontiguousarray(v_bits), k_pool_bits,
                              v_pool_bits, slot_mapping)
     return f32_to_bf16_bits(q_rot), k_new, v_new
+
+
+def add_rms_norm_ref(x_bits: np.ndarray, residual_bits: np.ndarray | None, weight_bits: np.ndarray,
+                     eps: float):
+    """Residual add + RMSNorm over the last axis, on bf16 bit patterns.
+
+    Returns (out_bits, residual_out_bits): out = bf16(bf16((x + r) * rsqrt(mean((x + r)^2) + eps))
+    * weight) with the sum in float32, and residual_out = bf16(x + r).  With residual None the
+    sum is x itself and residual_out is x.
+    """
+    x = bf16_bits_to_f32(x_bits)
+    if residual_bits is None:
+        s, resid = x, np.array(x_bits, dtype=np.uint16, copy=True)
+    else:
+        s = (x + bf16_bits_to_f32(residual_bits)).astype(np.float32)
+        resid = f32_to_bf16_bits(s)
+    var = np.mean(s * s, axis=-1, keepdims=True, dtype=np.float32)
+    r = (np.float32(1.0) / np.sqrt(var + np.float32(eps))).astype(np.float32)
+    normed = bf16_round(s * r)
+    out = bf16_round(normed * bf16_bits_to_f32(weight_bits))
+    return f32_to_bf16_bits(out), resid

@@ -72,3 +72,12 @@ def qk_norm_rope_store_bytes(slot_mapping, num_q_heads: int, num_kv_heads: int, 
             + 2 * head_dim * elem_bytes                                   # weights
             + t * num_q_heads * head_dim * elem_bytes                     # q out
             + written * 2 * num_kv_heads * head_dim * elem_bytes)         # k, v rows stored
+
+
+def add_rms_norm_bytes(num_tokens: int, hidden_size: int, elem_bytes: int, with_residual: bool = True) -> int:
+    """Fused residual add + RMSNorm: read the hidden state and the residual, write the
+    normalised output and the new residual (the weight vector once).  Without a residual:
+    read the hidden state, write the output."""
+    row = hidden_size * elem_bytes
+    per_token = 4 * row if with_residual else 2 * row
+    return num_tokens * per_token + row
