@@ -19,8 +19,8 @@ traffic = HBM bytes per decode call measured by rocprofv3 counters (FETCH_SIZE a
 WRITE_SIZE, calibrated on a plain copy of known size), read from
 profiles/decode_c2_counters.json when it was taken on the current decode sources.
 cpu_baseline = the float64 CPU oracle (store_ref + decode_ref) on the same C2 batch.
-decode_call / prefill_call = mean, median and minimum of the per-call event times; the
-prefill legs' headline time is the median call.
+decode_call / prefill_call / store_call = mean, median and minimum of the per-call event times; the
+prefill legs' headline times (the prefill and the store before it) are the median calls.
 Prefill legs are timed in steady state: after the warm-up calls, 10 calls are timed at once
 (cold_prefill_call), the matrix cores are then kept busy for settle_s seconds (the first
 tens of milliseconds of back-to-back MFMA work run slower while the engine clock
@@ -29,6 +29,8 @@ peaks = the spec peaks beside CUs x max engine clock x 4096 flop/clock (bf16 MFM
 device properties.
 qk_norm_rope_store = the fused q/k RMSNorm + rotary + KV store over C3's 16384 prompt
 tokens and C2's 64 decode tokens: algorithmic bytes / mean event time vs 8 TB/s.
+add_rms_norm = the fused residual add + RMSNorm over the same token counts' 4096-wide
+hidden rows (the norm in front of each block's projections), same figures.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu] [--no-prefill] [--no-c5]
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -223,12 +225,13 @@ def bench_prefill(dev, which, steps, warmup, settle_s=0.25):
             step()
         torch.cuda.synchronize()
     evs = timed(steps)
-    store_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    st_stats = stats_us([e[0].elapsed_time(e[1]) for e in evs])
     pf_stats = stats_us([e[1].elapsed_time(e[2]) for e in evs])
     # The median call: a rare stall of tens of milliseconds inside one timed interval (seen
-    # on some boxes, in either leg) would otherwise dominate the mean of 50 sub-ms calls;
-    # the mean stays in prefill_call.
+    # on some boxes, in either leg and in the store before it) would otherwise dominate the
+    # mean of 50 sub-ms calls; the means stay in prefill_call and store_call.
     pf_ms = pf_stats["median_us"] * 1e-3
+    store_ms = st_stats["median_us"] * 1e-3
     flops = acc.prefill_flops(case.cu_seqlens_q, case.cu_seqlens_k, sh.num_q_heads, sh.head_dim)
     st_bytes = acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
     tflops = flops / pf_ms / 1e9
@@ -237,7 +240,7 @@ def bench_prefill(dev, which, steps, warmup, settle_s=0.25):
     return {"workload": which, "prefill_us": round(pf_ms * 1e3, 2),
             "tflops": round(tflops, 2), "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "flop": flops, "prefill_call": pf_stats, "cold_prefill_call": cold,
-            "settle_s": settle_s, "store_us": round(store_ms * 1e3, 2),
+            "settle_s": settle_s, "store_us": round(store_ms * 1e3, 2), "store_call": st_stats,
             "store_gbs": round(st_bytes / store_ms / 1e6, 1)}
 
 
@@ -291,6 +294,41 @@ def bench_rope_store(dev, which, steps, warmup):
     log(f"[qk-norm+rope+store {which}] {t} tokens: {st['mean_us']:.1f} us -> {gbs:.0f} GB/s")
     return {"workload": f"{which} tokens ({t})", "call": st, "bytes": nbytes, "gbs": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def bench_add_rms_norm(dev, which, steps, warmup):
+    """Residual add + RMSNorm over the 4096-wide hidden rows of a leg's new tokens: C3's
+    16384 prompt tokens or C2's 64 decode tokens.  Inputs from workloads.norm_rows; out and
+    residual_out are separate buffers (the in-place form moves the same bytes)."""
+    import torch
+    import paged_kv_cache_258_amd as nkv
+    from paged_kv_cache_258_amd import accounting as acc
+    from paged_kv_cache_258_amd import workloads as wl
+
+    t = 16384 if which == "C3" else 64
+    h = wl.QWEN3_8B_HIDDEN
+    x, r, w = wl.norm_rows(t, h, wl.SEED_BASE + 78, dev)
+    out, res = torch.empty_like(x), torch.empty_like(x)
+
+    def call():
+        nkv.nkv_add_rms_norm(x, r, w, 1e-6, out=out, residual_out=res)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    st = stats_us([a.elapsed_time(b) for a, b in evs])
+    nbytes = acc.add_rms_norm_bytes(t, h, 2)
+    gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
+    log(f"[add+rmsnorm {which}] {t} x {h}: {st['mean_us']:.1f} us -> {gbs:.0f} GB/s")
+    return {"workload": f"{which} tokens ({t}) x hidden {h}", "call": st, "bytes": nbytes,
+            "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def bench_c5(dev, kind, reps, warmup):
@@ -525,6 +563,10 @@ def main():
     if not args.no_prefill:
         for which in ("C3", "C2"):
             rope_store.append(bench_rope_store(dev, which, args.steps, 3))
+    add_rms = []
+    if not args.no_prefill:
+        for which in ("C3", "C2"):
+            add_rms.append(bench_add_rms_norm(dev, which, args.steps, 3))
     long_decode = []
     if not args.no_c5:
         for kind in ("a", "b"):
@@ -578,6 +620,7 @@ def main():
                   "gbs": round(d["st_bytes"] / d["store_ms"] / 1e6, 1)},
         "prefill": prefill,
         "qk_norm_rope_store": rope_store,
+        "add_rms_norm": add_rms,
         "long_decode": long_decode,
         "cpu_baseline": cpu,
     }

@@ -16,6 +16,11 @@
  *   nkv_qk_norm_rope_store  q_norm(q), k_norm(k), rotary_emb(positions, q, k), then
  *                           store_kvcache(k, v, ...)
  *
+ * and the residual add + RMSNorm that feeds each decoder block's q/k/v projection
+ * (「同一个 Qwen3，两种写法」 §3.6, add_rms_forward):
+ *
+ *   nkv_add_rms_norm        x, residual = norm(x + residual), x + residual
+ *
  * Data layout (「同一个 Qwen3，两种写法」 §3.3, the pool allocated once at start-up):
  *   one layer's K pool and V pool are each a contiguous
  *   [num_blocks, block_size, num_kv_heads, head_dim] array, so a cache row ("slot")
@@ -29,7 +34,8 @@
  *   - every call is asynchronous and ordered on `stream` (a hipStream_t passed as
  *     void*, NULL = the legacy default stream); nothing is read back to the host;
  *   - attention never writes the pools; the store writes only the rows that
- *     slot_mapping names; `out` is fully overwritten and must not alias any input;
+ *     slot_mapping names; attention's `out` is fully overwritten and must not alias
+ *     any input (nkv_add_rms_norm alone may work in place, as stated there);
  *   - store before attention is the caller's job (the new token's K/V must be in the
  *     pool before the decode or prefix-cached prefill that reads it).
  *
@@ -155,6 +161,31 @@ nkv_status_t nkv_qk_norm_rope_store(const void* qkv, int64_t qkv_row_stride,
                                     void* q_out, void* k_cache, void* v_cache,
                                     int32_t num_blocks, int32_t block_size, nkv_dtype_t dtype,
                                     void* stream);
+
+/*
+ * Residual add + RMSNorm over token rows (bf16 only), the norm in front of each decoder
+ * block's projections.  「同一个 Qwen3，两种写法」 §3.6 (add_rms_forward; the plain
+ * RMSNorm when there is no residual).  For every row t, with float32 math:
+ *   s = x[t] + residual[t]              (s = x[t] when residual is NULL)
+ *   residual_out[t] = bf16(s)
+ *   n = bf16(s * rsqrt(mean(s*s) + eps)),  out[t] = bf16(n * weight)
+ * The norm is taken on the float32 sum, not on its bf16 copy.
+ *
+ *   x, residual    [num_tokens, hidden_size] bf16, contiguous rows, 16-byte aligned;
+ *                  residual may be NULL (the first block).
+ *   weight         [hidden_size] bf16, 16-byte aligned.
+ *   eps            RMSNorm epsilon in [0, 1] (Qwen3: 1e-6).
+ *   out            [num_tokens, hidden_size] bf16, 16-byte aligned.
+ *   residual_out   [num_tokens, hidden_size] bf16, 16-byte aligned, or NULL (not written).
+ *   hidden_size    a positive multiple of 8, at most 16384.
+ * In place: out may be x and residual_out may be residual (the very same pointer);
+ * any other overlap between an output and another buffer, and any overlap of out with
+ * residual_out, is rejected with NKV_ERR_INVALID_ARG.  dtype must be NKV_BF16
+ * (NKV_F32: NKV_ERR_UNSUPPORTED).  num_tokens == 0 is a no-op.
+ */
+nkv_status_t nkv_add_rms_norm(const void* x, const void* residual, const void* weight, float eps,
+                              int32_t num_tokens, int32_t hidden_size, void* out,
+                              void* residual_out, nkv_dtype_t dtype, void* stream);
 
 /*
  * Causal varlen prefill attention over the paged pools.

@@ -1,5 +1,6 @@
-"""Reference (oracle) for the step right before the KV store in a Qwen3 attention layer:
-per-head RMSNorm of q and k, rotary position embedding, then the store of k and v.
+"""Reference (oracle) for the step right before the KV store in a Qwen3 attention layer
+(per-head RMSNorm of q and k, rotary position embedding, then the store of k and v) and
+for the residual add + RMSNorm in front of each decoder block's projections.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/`` (and, like ``ref``, allowed in
 ``__graft_entry__.smoke()`` and bench.py's ``cpu_baseline`` leg); never by the product

@@ -1,5 +1,6 @@
 """nkv: the paged KV-cache data plane (store, paged prefill, paged decode, and the fused
-q/k norm + rotary + store before them) for MI355X.
+q/k norm + rotary + store before them, the residual add + RMSNorm in front of each
+block's projections) for MI355X.
 
 The compute lives in ``libnkv.so`` (HIP kernels for gfx950 behind the C ABI of
 ``include/nkv.h``); this package is its thin Python binding plus the seeded input
@@ -10,6 +11,7 @@ The library is loaded on first use and the calls raise if it is not built.
 from ._lib import (  # noqa: F401
     NkvError,
     load,
+    nkv_add_rms_norm,
     nkv_paged_attn_decode,
     nkv_paged_attn_decode_workspace_size,
     nkv_paged_attn_prefill,
@@ -22,6 +24,7 @@ __all__ = [
     "load",
     "nkv_store_kvcache",
     "nkv_qk_norm_rope_store",
+    "nkv_add_rms_norm",
     "nkv_paged_attn_prefill",
     "nkv_paged_attn_decode",
     "nkv_paged_attn_decode_workspace_size",

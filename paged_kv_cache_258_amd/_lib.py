@@ -26,6 +26,7 @@ EXPORTS = (
     "nkv_last_error",
     "nkv_store_kvcache",
     "nkv_qk_norm_rope_store",
+    "nkv_add_rms_norm",
     "nkv_paged_attn_prefill",
     "nkv_paged_attn_decode_workspace_size",
     "nkv_paged_attn_decode",
@@ -66,6 +67,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nkv_qk_norm_rope_store.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_i32, c_f, c_p, c_i32,
                                            c_i32, c_i32, c_i32, c_p, c_p, c_p, c_i32, c_i32,
                                            ctypes.c_int, c_p]
+    lib.nkv_add_rms_norm.restype = ctypes.c_int
+    lib.nkv_add_rms_norm.argtypes = [c_p, c_p, c_p, c_f, c_i32, c_i32, c_p, c_p, ctypes.c_int, c_p]
     lib.nkv_paged_attn_prefill.restype = ctypes.c_int
     lib.nkv_paged_attn_prefill.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i32,
                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
@@ -177,6 +180,35 @@ def nkv_qk_norm_rope_store(qkv: torch.Tensor, positions: torch.Tensor, q_norm_we
                                       _ptr(q_out), _ptr(k_cache), _ptr(v_cache), nb, bs, _dtype(qkv),
                                       _stream(qkv)), "nkv_qk_norm_rope_store")
     return q_out
+
+
+def nkv_add_rms_norm(x: torch.Tensor, residual: torch.Tensor | None, weight: torch.Tensor, eps: float,
+                     out: torch.Tensor | None = None, residual_out: torch.Tensor | None = None,
+                     write_residual: bool = True):
+    """Residual add + RMSNorm over the last axis; returns (out, residual_out).
+
+    x, residual: [..., H] bf16, contiguous (residual may be None: the plain RMSNorm, and the
+    new residual is x).  weight: [H] bf16.  out / residual_out may be given (out may be x,
+    residual_out may be residual: in place); with write_residual False and residual_out None
+    the new residual is not written and None is returned for it.
+    """
+    lib = load()
+    if not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be a contiguous [..., hidden] tensor")
+    h = x.shape[-1]
+    t = x.numel() // h if h else 0
+    for name, z in (("residual", residual), ("out", out), ("residual_out", residual_out)):
+        if z is not None and (z.shape != x.shape or not z.is_contiguous() or z.dtype != x.dtype):
+            raise ValueError(f"{name} must be a contiguous tensor of x's shape and dtype")
+    if weight.numel() != h or not weight.is_contiguous() or weight.dtype != x.dtype:
+        raise ValueError("weight must be a contiguous [hidden] tensor of x's dtype")
+    if out is None:
+        out = torch.empty_like(x)
+    if residual_out is None and write_residual:
+        residual_out = torch.empty_like(x)
+    _check(lib.nkv_add_rms_norm(_ptr(x), _ptr(residual), _ptr(weight), float(eps), t, h, _ptr(out),
+                                _ptr(residual_out), _dtype(x), _stream(x)), "nkv_add_rms_norm")
+    return out, residual_out
 
 
 def nkv_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

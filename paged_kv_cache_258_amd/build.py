@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnkv.so")
-SOURCES = ["api.hip", "store.hip", "rope_store.hip", "decode.hip", "prefill.hip", "validate.hip"]
+SOURCES = ["api.hip", "store.hip", "rope_store.hip", "rmsnorm.hip", "decode.hip", "prefill.hip", "validate.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -138,6 +138,13 @@ nkv_status_t checked(hipError_t e, const nkv::ValidateResult& r, const char* wha
   return NKV_OK;
 }
 
+// [a, a+na) and [b, b+nb) share a byte (null ranges share none)
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b) return false;
+  const auto pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + uintptr_t(nb) && pb < pa + uintptr_t(na);
+}
+
 }  // namespace
 
 NKV_EXPORT int nkv_abi_version(void) { return NKV_ABI_VERSION; }
@@ -233,6 +240,38 @@ NKV_EXPORT nkv_status_t nkv_qk_norm_rope_store(
   }
   return hip_status(nkv::launch_qk_norm_rope_store(a, static_cast<hipStream_t>(stream)),
                     "q/k norm + rotary + store launch");
+}
+
+NKV_EXPORT nkv_status_t nkv_add_rms_norm(const void* x, const void* residual, const void* weight,
+                                         float eps, int32_t num_tokens, int32_t hidden_size,
+                                         void* out, void* residual_out, nkv_dtype_t dtype,
+                                         void* stream) {
+  if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  if (dtype != NKV_BF16) return fail(NKV_ERR_UNSUPPORTED, "residual add + RMSNorm is implemented for bf16 only");
+  if (num_tokens < 0) return fail(NKV_ERR_INVALID_ARG, "num_tokens < 0");
+  if (hidden_size <= 0 || hidden_size % 8 != 0)
+    return fail(NKV_ERR_INVALID_ARG, "hidden_size must be a positive multiple of 8");
+  if (hidden_size > nkv::kAddRmsNormMaxHidden)
+    return fail(NKV_ERR_UNSUPPORTED, "hidden_size %d above %d", hidden_size, nkv::kAddRmsNormMaxHidden);
+  if (!(eps >= 0.0f) || eps > 1.0f) return fail(NKV_ERR_INVALID_ARG, "eps must lie in [0, 1]");
+  if (num_tokens == 0) return ok();
+  if (!x || !weight || !out) return fail(NKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(x) || !aligned16(residual) || !aligned16(weight) || !aligned16(out) ||
+      !aligned16(residual_out))
+    return fail(NKV_ERR_INVALID_ARG, "x, residual, weight, out and residual_out need 16-byte alignment");
+  // each output is either the very same rows as an input (in place) or apart from every
+  // other buffer
+  const int64_t n = int64_t(num_tokens) * hidden_size * 2;
+  const int64_t nw = int64_t(hidden_size) * 2;
+  if (overlaps(out, n, residual_out, n)) return fail(NKV_ERR_INVALID_ARG, "out and residual_out overlap");
+  for (void* o : {out, residual_out}) {
+    if ((o != x && overlaps(o, n, x, n)) || (o != residual && overlaps(o, n, residual, n)) ||
+        overlaps(o, n, weight, nw))
+      return fail(NKV_ERR_INVALID_ARG, "an output overlaps an input other than as the same rows");
+  }
+  nkv::AddRmsNormArgs a{x, residual, weight, eps, num_tokens, hidden_size, out, residual_out, num_cus()};
+  return hip_status(nkv::launch_add_rms_norm(a, static_cast<hipStream_t>(stream)),
+                    "residual add + RMSNorm launch");
 }
 
 NKV_EXPORT nkv_status_t nkv_paged_attn_prefill(

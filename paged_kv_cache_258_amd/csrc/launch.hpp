@@ -45,6 +45,22 @@ struct RopeStoreArgs {
 };
 hipError_t launch_qk_norm_rope_store(const RopeStoreArgs& a, hipStream_t st);
 
+// Residual add + RMSNorm over contiguous [num_tokens, hidden] bf16 rows.  residual and
+// residual_out may be null; out may equal x and residual_out may equal residual.
+struct AddRmsNormArgs {
+  const void* x;
+  const void* residual;
+  const void* weight;
+  float eps;
+  int32_t num_tokens;
+  int32_t hidden;
+  void* out;
+  void* residual_out;
+  int num_cus;
+};
+hipError_t launch_add_rms_norm(const AddRmsNormArgs& a, hipStream_t st);
+constexpr int32_t kAddRmsNormMaxHidden = 16384;
+
 struct PagedArgs {
   const void* k_cache;
   const void* v_cache;

@@ -385,3 +385,31 @@ def c5_decode(kind: str, device="cpu", layers=None, seed_k=None, shape=QWEN3_8B,
     return MultiLayerDecode(f"C5{kind}-decode", shape, lens, out,
                             meta={"num_blocks": nb, "sum_context": int(lens.sum()),
                                   "layers": list(layer_ids), "seed": seed})
+
+
+# --------------------------------------------------------------------------------------
+# residual add + RMSNorm rows
+# --------------------------------------------------------------------------------------
+
+QWEN3_8B_HIDDEN = 4096
+
+
+def norm_rows(num_tokens: int, hidden: int = QWEN3_8B_HIDDEN, seed: int = 6, device="cpu",
+              with_residual: bool = True):
+    """Inputs of one residual add + RMSNorm call: (x, residual or None, weight), bf16.
+
+    x is a block output: N(0, 1) times a per-token scale drawn log-uniformly in [1e-2, 30];
+    the residual stream is N(0, 1) times a per-token scale log-uniform in [1e-1, 1e2] (it
+    grows over the layers); the weight is 1 + 0.1 N(0, 1).  Everything is drawn from one
+    seeded generator on ``device``.
+    """
+    gen = _torch_gen(device, seed)
+    def scale(lo, hi):
+        u = torch.rand((num_tokens, 1), generator=gen, device=device, dtype=torch.float32)
+        return torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))
+    x = (randn((num_tokens, hidden), gen, device, "f32") * scale(1e-2, 30.0)).to(torch.bfloat16)
+    r = None
+    if with_residual:
+        r = (randn((num_tokens, hidden), gen, device, "f32") * scale(1e-1, 1e2)).to(torch.bfloat16)
+    w = (1.0 + 0.1 * randn((hidden,), gen, device, "f32")).to(torch.bfloat16)
+    return x, r, w

@@ -189,3 +189,44 @@ def test_rope_store_rejects(lib, kw, status):
 
 def test_rope_store_zero_tokens_is_noop(lib):
     assert rope_store(lib, n=0, qkv=None, pos=None, slots=None, qout=None, kc=None, vc=None) == _lib.NKV_OK
+
+
+# distinct fake buffers 1 MiB apart: a [4, 4096] bf16 row block is 32 KiB
+X_, R_, W_, O_, RO_ = (0x100000 * i for i in range(1, 6))
+
+
+def add_rms(lib, **kw):
+    a = dict(x=X_, r=R_, w=W_, eps=1e-6, n=4, h=4096, out=O_, ro=RO_, dtype=1, stream=None)
+    a.update(kw)
+    return lib.nkv_add_rms_norm(a["x"], a["r"], a["w"], a["eps"], a["n"], a["h"], a["out"],
+                                a["ro"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), _lib.NKV_ERR_UNSUPPORTED),          # fp32: bf16 only
+    (dict(dtype=7), _lib.NKV_ERR_INVALID_ARG),
+    (dict(h=0), _lib.NKV_ERR_INVALID_ARG),
+    (dict(h=4100), _lib.NKV_ERR_INVALID_ARG),           # not a multiple of 8
+    (dict(h=16392), _lib.NKV_ERR_UNSUPPORTED),          # above the widest row
+    (dict(n=-1), _lib.NKV_ERR_INVALID_ARG),
+    (dict(eps=2.0), _lib.NKV_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), _lib.NKV_ERR_INVALID_ARG),
+    (dict(x=None), _lib.NKV_ERR_INVALID_ARG),
+    (dict(w=None), _lib.NKV_ERR_INVALID_ARG),
+    (dict(out=None), _lib.NKV_ERR_INVALID_ARG),
+    (dict(x=X_ + 8), _lib.NKV_ERR_INVALID_ARG),         # 16-byte alignment
+    (dict(ro=RO_ + 8), _lib.NKV_ERR_INVALID_ARG),
+    (dict(out=RO_), _lib.NKV_ERR_INVALID_ARG),          # out is residual_out
+    (dict(out=RO_ + 4096), _lib.NKV_ERR_INVALID_ARG),   # out overlaps residual_out
+    (dict(out=X_ + 16), _lib.NKV_ERR_INVALID_ARG),      # shifted onto x: not in place
+    (dict(ro=R_ - 16), _lib.NKV_ERR_INVALID_ARG),       # shifted onto residual
+    (dict(out=R_ + 64), _lib.NKV_ERR_INVALID_ARG),
+    (dict(ro=W_), _lib.NKV_ERR_INVALID_ARG),            # output on top of the weight
+])
+def test_add_rms_norm_rejects(lib, kw, status):
+    assert add_rms(lib, **kw) == status
+    assert lib.nkv_last_error() != b""
+
+
+def test_add_rms_norm_zero_tokens_is_noop(lib):
+    assert add_rms(lib, n=0, x=None, r=None, w=None, out=None, ro=None) == _lib.NKV_OK

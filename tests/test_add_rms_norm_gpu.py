@@ -1,0 +1,108 @@
+"""Parity of nkv_add_rms_norm (residual add + RMSNorm, bf16) with the oracle
+oracle/rope_norm.add_rms_norm_ref on the same seeded inputs.
+
+The new residual bf16(x + residual) is one float32 add and one rounding on both sides, so
+it must match bit for bit.  The normalised output takes the same rounding points on both
+sides (cast to bf16 after the normalisation and after the weight product, float32 in
+between); what can still differ is the summation order of the row's mean square and the
+last bit of the reciprocal root, which moves an element across a bf16 rounding boundary
+now and then.  The bar: at least 99.5% of output elements bit-identical, and every
+difference within 2^-6 of the largest |output| of its row (two bf16 units at that scale).
+
+Inputs (paged_kv_cache_258_amd.workloads.norm_rows): block outputs N(0, 1) times a per-row
+scale log-uniform in [1e-2, 30], residual rows N(0, 1) times a per-row scale log-uniform
+in [1e-1, 1e2], weight 1 + 0.1 N(0, 1).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import rope_norm as rn
+from paged_kv_cache_258_amd import nkv_add_rms_norm
+from paged_kv_cache_258_amd import workloads as wl
+
+from _gpu_helpers import host_bits, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+def check(got_out, got_res, x_bits, r_bits, w_bits, what, res_written=True):
+    want_out, want_res = rn.add_rms_norm_ref(x_bits, r_bits, w_bits, EPS)
+    if res_written:
+        assert np.array_equal(got_res, want_res), f"{what}: new residual differs"
+    g, w = rn.bf16_bits_to_f32(got_out), rn.bf16_bits_to_f32(want_out)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    same = float(np.mean(got_out == want_out))
+    err = np.abs(g.astype(np.float64) - w.astype(np.float64))
+    bound = (2.0 ** -6) * np.abs(w).max(axis=-1, keepdims=True)
+    worst = float((err / np.maximum(bound, 1e-30)).max()) if err.size else 0.0
+    log(f"  {what}: bit-identical {same:.5f}, worst error / bound {worst:.3f}")
+    assert same >= 0.995, f"{what}: only {same:.5f} of elements bit-identical"
+    assert np.all(err <= bound), f"{what}: error beyond two bf16 units of the row scale"
+
+
+def run(t, h, seed, with_residual=True):
+    dev = require_gpu()
+    log(f"[add_rms_norm] T={t} H={h} residual={with_residual} seed={seed}")
+    x, r, w = wl.norm_rows(t, h, seed, dev, with_residual)
+    out, res = nkv_add_rms_norm(x, r, w, EPS)
+    torch.cuda.synchronize()
+    check(host_bits(out), host_bits(res), host_bits(x), None if r is None else host_bits(r),
+          host_bits(w), f"T={t} H={h}")
+
+
+@pytest.mark.parametrize("t,h", [(300, 4096), (64, 4096), (37, 1024), (1, 8), (5, 1000),
+                                 (33, 5120), (7, 16384), (129, 2056)])
+def test_add_rms_norm_matches_oracle(t, h):
+    # 1000, 5120, 2056: rows that leave part of the last 256-chunk pass idle
+    run(t, h, 700 + t + h)
+
+
+@pytest.mark.parametrize("t,h", [(50, 4096), (3, 1000)])
+def test_rms_norm_without_residual(t, h):
+    # the first block: the plain RMSNorm of x, and x itself is the new residual
+    run(t, h, 760 + t, with_residual=False)
+
+
+def test_add_rms_norm_prefill_sized_batch():
+    # 16384 tokens x 4096: the 8 x 2048-token prefill's hidden states
+    run(16384, 4096, 790)
+
+
+def test_add_rms_norm_in_place():
+    # out written over x, the new residual over the residual (the in-place use)
+    dev = require_gpu()
+    x, r, w = wl.norm_rows(200, 4096, 800, dev)
+    x_bits, r_bits = host_bits(x), host_bits(r)
+    out, res = nkv_add_rms_norm(x, r, w, EPS, out=x, residual_out=r)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == x.data_ptr() and res.data_ptr() == r.data_ptr()
+    check(host_bits(x), host_bits(r), x_bits, r_bits, host_bits(w), "in place")
+
+
+def test_add_rms_norm_residual_not_written_and_zero_rows():
+    # residual_out NULL: nothing but out is written; an all-zero row normalises to zero
+    dev = require_gpu()
+    x, r, w = wl.norm_rows(40, 4096, 810, dev)
+    x[:3] = 0
+    r[:3] = 0
+    r_before = host_bits(r)
+    out, res = nkv_add_rms_norm(x, r, w, EPS, write_residual=False)
+    torch.cuda.synchronize()
+    assert res is None
+    assert np.array_equal(host_bits(r), r_before)
+    check(host_bits(out), None, host_bits(x), r_before, host_bits(w), "no residual_out",
+          res_written=False)
+    assert bool((out[:3] == 0).all())
+
+
+def test_add_rms_norm_zero_tokens():
+    dev = require_gpu()
+    x = torch.empty((0, 4096), dtype=torch.bfloat16, device=dev)
+    w = torch.ones(4096, dtype=torch.bfloat16, device=dev)
+    out, res = nkv_add_rms_norm(x, x, w, EPS)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 4096) and res.shape == (0, 4096)

@@ -5,6 +5,7 @@ rotate_half form), and invariants of the rotation.
 """
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import rope_norm as rn
@@ -184,3 +185,23 @@ def test_add_rms_norm_hand_worked_and_reductions():
     via_rounded = rn.f32_to_bf16_bits(rn.rms_norm_ref(rn.bf16_bits_to_f32(res_s), rn.bf16_bits_to_f32(w), 1e-6))
     assert not np.array_equal(out_s, via_rounded)
     assert np.mean(out_s == via_rounded) > 0.5          # yet close: mostly the same bits
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_add_rms_norm_within_two_roundings_of_float64(eps):
+    # The definition written in float64: s = x + r, out = s / sqrt(mean(s^2) + eps) * w.
+    # The oracle rounds to bf16 twice (after the norm, after the weight); each rounding is
+    # within 2^-8 relative (8 significant bits, to nearest), so out stays within
+    # (1 + 2^-8)^2 - 1 = 2^-7 + 2^-16 of the float64 value, element by element (the float32
+    # sum and mean add ~2^-22).  A dropped eps, a wrong divisor of the mean or a missing
+    # residual moves elements much further.
+    rng = np.random.default_rng(33)
+    h = 512
+    x = rn.f32_to_bf16_bits((rng.standard_normal((8, h)) * np.exp(rng.uniform(-3, 2, (8, 1)))).astype(np.float32))
+    r = rn.f32_to_bf16_bits((rng.standard_normal((8, h)) * np.exp(rng.uniform(-3, 2, (8, 1)))).astype(np.float32))
+    w = rn.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(h)).astype(np.float32))
+    out, _ = rn.add_rms_norm_ref(x, r, w, eps)
+    s = rn.bf16_bits_to_f32(x).astype(np.float64) + rn.bf16_bits_to_f32(r).astype(np.float64)
+    want = s / np.sqrt(np.mean(s * s, axis=-1, keepdims=True) + eps) * rn.bf16_bits_to_f32(w).astype(np.float64)
+    got = rn.bf16_bits_to_f32(out).astype(np.float64)
+    assert np.all(np.abs(got - want) <= (2.0 ** -7 + 2.0 ** -12) * np.abs(want) + 1e-30)
