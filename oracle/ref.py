@@ -25,6 +25,11 @@ What is computed, and where the pages define it:
 * ``decode_ref`` -- ``flash_attn_with_kvcache(q.unsqueeze(1), ..., cache_seqlens=
   context_lens, block_table=...)``: one query per sequence against its cached
   keys (same sources).  Written as its own loop, independent of ``prefill_ref``.
+* ``varlen_prefill_ref`` -- the branch without a prefix cache,
+  ``flash_attn_varlen_func(q, k, v, cu_seqlens_q/k, ..., causal=True)`` with the
+  fresh k and v (「Nano-vLLM深度解读（下）」 §4: no block table when nothing is
+  cached): sequence ``b``'s keys are rows ``cu_seqlens_k[b]..cu_seqlens_k[b+1]`` of
+  the flat ``[Tk, Hkv, D]`` k and v (「同一个 Qwen3，两种写法」 §3.2).
 
 Readings where the pages are silent (each listed with its reason in the design doc):
   * causal alignment when a chunk has fewer queries than keys: bottom-right --
@@ -50,6 +55,7 @@ __all__ = [
     "gather",
     "attn",
     "prefill_ref",
+    "varlen_prefill_ref",
     "decode_ref",
 ]
 
@@ -213,6 +219,25 @@ def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         kb = as_f64(gather(k_pool, block_table[b], lk), elem)
         vb = as_f64(gather(v_pool, block_table[b], lk), elem)
         out[q0:q1] = attn(as_f64(q[q0:q1], elem), kb, vb, scale)
+    return out
+
+
+def varlen_prefill_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_q: np.ndarray,
+                       cu_seqlens_k: np.ndarray, scale: float, elem: str = "f64") -> np.ndarray:
+    """Causal varlen prefill over contiguous K/V (no block table).
+
+    q    : [Tq, Hq, D];  k, v : [Tk, Hkv, D] (element type ``elem``)
+    Sequence b's queries are rows ``cu_q[b]:cu_q[b+1]`` of q and its keys rows
+    ``cu_k[b]:cu_k[b+1]`` of k and v.  Returns float64 out [Tq, Hq, D].
+    """
+    tq, hq, d = q.shape
+    out = np.zeros((tq, hq, d), dtype=np.float64)
+    for b in range(len(cu_seqlens_q) - 1):
+        q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
+        if q1 == q0:
+            continue
+        out[q0:q1] = attn(as_f64(q[q0:q1], elem), as_f64(k[k0:k1], elem), as_f64(v[k0:k1], elem), scale)
     return out
 
 

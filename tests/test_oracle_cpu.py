@@ -249,6 +249,33 @@ def _random_paged_case(seed, seqs, hq=4, hkv=2, d=8, bs=4, spare_blocks=3):
 
 
 @pytest.mark.parametrize("seed,seqs,hq,hkv", [
+    (20, [(3, 3), (2, 2), (2, 2)], 4, 2),
+    (21, [(5, 13), (1, 9), (7, 7), (0, 4)], 4, 1),
+    (22, [(9, 9), (4, 10)], 6, 3),
+])
+def test_varlen_prefill_matches_brute_force_and_paged(seed, seqs, hq, hkv):
+    # contiguous K/V: the dense masked brute force over the flat batch, and the paged
+    # oracle on the same keys scattered into shuffled blocks
+    c = _random_paged_case(seed, seqs, hq=hq, hkv=hkv)
+    scale = 1 / math.sqrt(8)
+    got = ref.varlen_prefill_ref(c["q"], c["k_all"], c["v_all"], c["cu_q"], c["cu_k"], scale)
+    want = brute.brute_attention(c["q"], c["k_all"], c["v_all"],
+                                 [s[0] for s in seqs], [s[1] for s in seqs], scale)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    paged = ref.prefill_ref(c["q"], c["kp"], c["vp"], c["cu_q"], c["cu_k"], c["table"], scale)
+    assert np.array_equal(got, paged)
+
+
+def test_varlen_prefill_reads_only_its_rows():
+    # rows outside every sequence's key range (NaN) never reach an output
+    c = _random_paged_case(23, [(4, 6), (3, 3)], hq=4, hkv=2)
+    k = np.concatenate([c["k_all"], np.full((5,) + c["k_all"].shape[1:], np.nan)])
+    v = np.concatenate([c["v_all"], np.full((5,) + c["v_all"].shape[1:], np.nan)])
+    got = ref.varlen_prefill_ref(c["q"], k, v, c["cu_q"], c["cu_k"], 0.3)
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("seed,seqs,hq,hkv", [
     (10, [(3, 3), (2, 2), (2, 2)], 4, 2),
     (11, [(5, 13), (1, 9), (7, 7), (0, 4)], 4, 1),
     (12, [(9, 9), (4, 10)], 6, 3),
