@@ -10,6 +10,8 @@
  *   nkv_paged_attn_decode   flash_attn_with_kvcache(q.unsqueeze(1), k_cache, v_cache,
  *                           cache_seqlens=context_lens, block_table, softmax_scale,
  *                           causal=True)
+ *   nkv_attn_varlen_prefill flash_attn_varlen_func(q, k, v, cu_seqlens_q/k, max_seqlen_q/k,
+ *                           softmax_scale, causal=True)   (no prefix cache: fresh k, v)
  *
  * and the step right before the store in Qwen3Attention.forward (same page, §2), fused:
  *
@@ -33,6 +35,10 @@
  *     between calls (it caches the device's compute-unit count per device);
  *   - every call is asynchronous and ordered on `stream` (a hipStream_t passed as
  *     void*, NULL = the legacy default stream); nothing is read back to the host;
+ *   - outside checking mode a call allocates nothing, issues no memset and never
+ *     synchronises, so it can be captured into a HIP graph (stream capture) and
+ *     replayed; the decode work split is derived on the device from context_lens, so
+ *     a captured decode stays valid while the lengths in that buffer change;
  *   - attention never writes the pools; the store writes only the rows that
  *     slot_mapping names; attention's `out` is fully overwritten and must not alias
  *     any input (nkv_add_rms_norm alone may work in place, as stated there);
@@ -220,6 +226,35 @@ nkv_status_t nkv_paged_attn_prefill(const void* q, int64_t q_row_stride,
                                     int32_t num_blocks, int32_t block_size,
                                     float softmax_scale, nkv_dtype_t dtype,
                                     void* out, void* stream);
+
+/*
+ * Causal varlen prefill over contiguous K/V: the branch without a prefix cache, where
+ * attention reads the fresh k and v of this call instead of the pools.
+ * 「Nano-vLLM深度解读（下）」 §4 (attention.py: flash_attn_varlen_func(q, k, v, ...) when
+ * no block table is set); 「同一个 Qwen3，两种写法」 §3.2 (flat batch split by cu_seqlens).
+ * Same operation as nkv_paged_attn_prefill, except that sequence b's keys are rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v.
+ *
+ *   q      [total_q, num_q_heads, head_dim], rows q_row_stride elements apart.
+ *   k, v   [total_k, num_kv_heads, head_dim], rows k_row_stride / v_row_stride elements
+ *          apart (>= num_kv_heads*head_dim; e.g. views of a packed qkv projection).
+ *          Strides are multiples of 16 bytes; q, k, v, out 16-byte aligned.
+ *   out    [total_q, num_q_heads, head_dim] contiguous, dtype of q; must not alias an input.
+ *   cu_seqlens_q, cu_seqlens_k  [num_seqs+1] int32 running sums from 0, Lq <= Lk per
+ *          sequence, cu_seqlens_q[num_seqs] = total_q, cu_seqlens_k[num_seqs] <= total_k.
+ *   max_seqlen_q <= max_seqlen_k <= total_k: host upper bounds (size the grid).
+ *   Supported: head_dim 64 or 128; num_q_heads/num_kv_heads in {1,2,4,8}; bf16 (MFMA
+ *   path) or fp32 (VALU path).  num_seqs, total_q or max_seqlen_q == 0: a no-op.
+ * Preconditions checked in checking mode: the cu_seqlens conditions above.
+ */
+nkv_status_t nkv_attn_varlen_prefill(const void* q, int64_t q_row_stride, const void* k,
+                                     int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     float softmax_scale, nkv_dtype_t dtype, void* out,
+                                     void* stream);
 
 /*
  * Bytes of device workspace nkv_paged_attn_decode needs for these sizes (partial

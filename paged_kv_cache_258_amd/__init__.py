@@ -1,4 +1,5 @@
-"""nkv: the paged KV-cache data plane (store, paged prefill, paged decode, and the fused
+"""nkv: the paged KV-cache data plane (store, paged prefill, paged decode, prefill over
+contiguous K/V for the no-prefix-cache branch, and the fused
 q/k norm + rotary + store before them, the residual add + RMSNorm in front of each
 block's projections) for MI355X.
 
@@ -12,6 +13,7 @@ from ._lib import (  # noqa: F401
     NkvError,
     load,
     nkv_add_rms_norm,
+    nkv_attn_varlen_prefill,
     nkv_paged_attn_decode,
     nkv_paged_attn_decode_workspace_size,
     nkv_paged_attn_prefill,
@@ -26,6 +28,7 @@ __all__ = [
     "nkv_qk_norm_rope_store",
     "nkv_add_rms_norm",
     "nkv_paged_attn_prefill",
+    "nkv_attn_varlen_prefill",
     "nkv_paged_attn_decode",
     "nkv_paged_attn_decode_workspace_size",
 ]

@@ -28,6 +28,7 @@ EXPORTS = (
     "nkv_qk_norm_rope_store",
     "nkv_add_rms_norm",
     "nkv_paged_attn_prefill",
+    "nkv_attn_varlen_prefill",
     "nkv_paged_attn_decode_workspace_size",
     "nkv_paged_attn_decode",
 )
@@ -73,6 +74,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nkv_paged_attn_prefill.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_i32,
                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                            c_i32, c_i32, c_f, ctypes.c_int, c_p, c_p]
+    lib.nkv_attn_varlen_prefill.restype = ctypes.c_int
+    lib.nkv_attn_varlen_prefill.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p, c_p, c_i32, c_i32,
+                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f,
+                                            ctypes.c_int, c_p, c_p]
     lib.nkv_paged_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.nkv_paged_attn_decode_workspace_size.argtypes = [c_i32] * 6
     lib.nkv_paged_attn_decode.restype = ctypes.c_int
@@ -239,6 +244,38 @@ def nkv_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                       int(max_seqlen_k), hq, hkv, d, nb, bs, float(softmax_scale),
                                       _dtype(q), _ptr(out), _stream(q)),
            "nkv_paged_attn_prefill")
+    return out
+
+
+def nkv_attn_varlen_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                            cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                            softmax_scale: float, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal varlen prefill over contiguous k/v [Tk, Hkv, D] (rows may be strided views);
+    returns out [Tq, Hq, D]."""
+    lib = load()
+    tq, hq, d = q.shape
+    tk, hkv, kd = k.shape
+    if v.shape != k.shape or kd != d:
+        raise ValueError("k and v must be [Tk, Hkv, D] with q's head_dim")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{name} needs contiguous [H, D] rows")
+        if t.dtype != q.dtype:
+            raise ValueError("q, k and v must share a dtype")
+    _int32_dev(cu_seqlens_q, "cu_seqlens_q")
+    _int32_dev(cu_seqlens_k, "cu_seqlens_k")
+    nseq = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != nseq + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=q.dtype, device=q.device)
+    elif out.shape != (tq, hq, d) or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous [Tq, Hq, D] tensor of q's dtype")
+    _check(lib.nkv_attn_varlen_prefill(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+                                       _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseq, tq, tk,
+                                       int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
+                                       float(softmax_scale), _dtype(q), _ptr(out), _stream(q)),
+           "nkv_attn_varlen_prefill")
     return out
 
 

@@ -301,6 +301,7 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_prefill(
   if (!aligned16(q) || !aligned16(out)) return fail(NKV_ERR_INVALID_ARG, "q/out must be 16-byte aligned");
   a.q = q;
   a.q_row_elems = q_row_stride;
+  a.k_row_elems = a.v_row_elems = int64_t(num_kv_heads) * head_dim;
   a.cu_seqlens_q = cu_seqlens_q;
   a.cu_seqlens_k = cu_seqlens_k;
   a.max_seqlen_q = max_seqlen_q;
@@ -308,11 +309,77 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_prefill(
   a.out = out;
   if (validating()) {
     nkv::ValidateResult r{};
-    const hipError_t e = nkv::validate_prefill(a, total_q, num_blocks, static_cast<hipStream_t>(stream), &r);
+    const hipError_t e = nkv::validate_prefill(a, total_q, -1, num_blocks, static_cast<hipStream_t>(stream), &r);
     const nkv_status_t vs = checked(e, r, "nkv_paged_attn_prefill");
     if (vs != NKV_OK) return vs;
   }
   return hip_status(nkv::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+NKV_EXPORT nkv_status_t nkv_attn_varlen_prefill(
+    const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride, const void* v,
+    int64_t v_row_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+    int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, float softmax_scale, nkv_dtype_t dtype, void* out,
+    void* stream) {
+  if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(NKV_ERR_INVALID_ARG, "negative size");
+  if (num_q_heads <= 0 || num_kv_heads <= 0) return fail(NKV_ERR_INVALID_ARG, "head counts must be positive");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(NKV_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  const int grp = num_q_heads / num_kv_heads;
+  if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
+    return fail(NKV_ERR_UNSUPPORTED, "GQA group size %d not in {1,2,4,8}", grp);
+  if (head_dim != 64 && head_dim != 128) return fail(NKV_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  if (!(softmax_scale == softmax_scale) || softmax_scale < 0.f)
+    return fail(NKV_ERR_INVALID_ARG, "softmax_scale must be a non-negative number");
+  if (max_seqlen_q > max_seqlen_k)
+    return fail(NKV_ERR_INVALID_ARG, "max_seqlen_q (%d) > max_seqlen_k (%d)", max_seqlen_q, max_seqlen_k);
+  if (max_seqlen_k > total_k) return fail(NKV_ERR_INVALID_ARG, "max_seqlen_k exceeds total_k");
+  const int eb = elem_bytes(dtype);
+  const int64_t qrow = int64_t(num_q_heads) * head_dim, kvrow = int64_t(num_kv_heads) * head_dim;
+  if (q_row_stride < qrow) return fail(NKV_ERR_INVALID_ARG, "q_row_stride below num_q_heads*head_dim");
+  if (k_row_stride < kvrow || v_row_stride < kvrow)
+    return fail(NKV_ERR_INVALID_ARG, "k/v row stride below num_kv_heads*head_dim");
+  if ((q_row_stride * eb) % 16 != 0 || (k_row_stride * eb) % 16 != 0 || (v_row_stride * eb) % 16 != 0)
+    return fail(NKV_ERR_INVALID_ARG, "row strides must be multiples of 16 bytes");
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(NKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(NKV_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  nkv::PrefillArgs a{};
+  a.p.k_cache = k;
+  a.p.v_cache = v;
+  a.p.block_table = nullptr;                 // contiguous keys: rows cu_seqlens_k[b] ..
+  a.p.max_blocks_per_seq = 0;
+  a.p.num_seqs = num_seqs;
+  a.p.num_q_heads = num_q_heads;
+  a.p.num_kv_heads = num_kv_heads;
+  a.p.head_dim = head_dim;
+  a.p.block_size = 1 << 10;
+  a.p.log2_block_size = 10;                  // unused without a block table
+  a.p.scale_log2e = softmax_scale * 1.4426950408889634f;
+  a.p.dtype = dtype == NKV_BF16 ? nkv::Dtype::BF16 : nkv::Dtype::F32;
+  a.p.num_cus = num_cus();
+  a.q = q;
+  a.q_row_elems = q_row_stride;
+  a.k_row_elems = k_row_stride;
+  a.v_row_elems = v_row_stride;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.max_seqlen_q = max_seqlen_q;
+  a.max_seqlen_k = max_seqlen_k;
+  a.out = out;
+  if (validating()) {
+    nkv::ValidateResult r{};
+    const hipError_t e = nkv::validate_prefill(a, total_q, total_k, 0, static_cast<hipStream_t>(stream), &r);
+    const nkv_status_t vs = checked(e, r, "nkv_attn_varlen_prefill");
+    if (vs != NKV_OK) return vs;
+  }
+  return hip_status(nkv::launch_prefill(a, static_cast<hipStream_t>(stream)), "varlen prefill launch");
 }
 
 NKV_EXPORT size_t nkv_paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,

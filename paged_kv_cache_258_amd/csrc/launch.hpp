@@ -77,10 +77,15 @@ struct PagedArgs {
   int num_cus;
 };
 
+// Prefill over the paged pools, or (p.block_table == nullptr) over contiguous varlen K/V:
+// sequence b's keys are rows cu_seqlens_k[b] .. cu_seqlens_k[b+1] of k/v (p.k_cache /
+// p.v_cache), rows k_row_elems / v_row_elems elements apart.  Paged: both Hkv * D.
 struct PrefillArgs {
   PagedArgs p;
   const void* q;
   int64_t q_row_elems;
+  int64_t k_row_elems;
+  int64_t v_row_elems;
   const int32_t* cu_seqlens_q;
   const int32_t* cu_seqlens_k;
   int32_t max_seqlen_q;
@@ -130,8 +135,9 @@ struct ValidateResult {
 };
 hipError_t validate_store(const int32_t* slots, int32_t n, int64_t rows, hipStream_t st,
                           ValidateResult* r);
-hipError_t validate_prefill(const PrefillArgs& a, int32_t total_q, int32_t num_blocks,
-                            hipStream_t st, ValidateResult* r);
+// total_k: rows of contiguous K/V (no block table), or -1 for the paged pools.
+hipError_t validate_prefill(const PrefillArgs& a, int32_t total_q, int32_t total_k,
+                            int32_t num_blocks, hipStream_t st, ValidateResult* r);
 hipError_t validate_decode(const DecodeArgs& a, int32_t num_blocks, hipStream_t st,
                            ValidateResult* r);
 

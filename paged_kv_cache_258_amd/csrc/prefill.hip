@@ -91,6 +91,7 @@ template <int D, int G, int QB>
 __global__ void __launch_bounds__(8 / QB * 64)
 prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+                    int64_t k_stride, int64_t v_stride,
                     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                     const int32_t* __restrict__ block_table, int32_t max_blocks,
                     int32_t num_kv_heads, int32_t log2_bs, float scale_log2e,
@@ -123,11 +124,14 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int kend = diag + min(q0 + Geo::BQ, lq);      // keys the workgroup needs
   const int ntiles = (kend + kBK - 1) / kBK;
   const int wkend = wq0 < lq ? diag + min(wq0 + WQ, lq) : 0;   // keys this wave needs
-  const int32_t* __restrict__ trow = block_table + int64_t(b) * max_blocks;
+  // paged: keys through the block table; otherwise rows kv0.. of contiguous k/v
+  const bool paged = block_table != nullptr;
+  const int64_t kv0 = paged ? 0 : cu_k[b];
+  const int32_t* __restrict__ trow = paged ? block_table + int64_t(b) * max_blocks : nullptr;
   const int bs_mask = (1 << log2_bs) - 1;
   const int last_blk = (lk > 0 ? lk - 1 : 0) >> log2_bs;
   const int ids_per_tile = log2_bs >= kLog2BK ? 1 : (kBK >> log2_bs);
-  const int64_t row_elems = int64_t(num_kv_heads) * D;
+  const int64_t row_elems = int64_t(num_kv_heads) * D;   // pool row
   const uint16_t* kbase = k_cache + int64_t(g) * D;
   const uint16_t* vbase = v_cache + int64_t(g) * D;
 
@@ -147,7 +151,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
 
   // ---- copies: block ids two tiles ahead (LDS), K rows by DMA, V through registers ----
   auto issue_ids = [&](int t) {                       // wave 0: ids of tile t -> s_ids[t % 3]
-    if (wave == 0 && lane < ids_per_tile) {
+    if (paged && wave == 0 && lane < ids_per_tile) {
       const int blk = min(((t * kBK) >> log2_bs) + lane, last_blk);
       load_lds4(trow + blk, &s_ids[t % 3][0]);
     }
@@ -164,20 +168,22 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     k_elem[j] = ((s % CPR) ^ (k_row[j] & (CPR - 1))) * 8;
   }
   // With block_size >= kBK a tile lies inside one physical block: its base is uniform
-  // (one LDS read, scalar math) and each lane adds only row * row_elems.
-  const bool tile_in_block = log2_bs >= kLog2BK;
-  auto tile_base = [&](int t, const uint16_t* base) {
+  // (one LDS read, scalar math) and each lane adds only row * stride.  Contiguous K/V is
+  // one such "block".
+  const bool tile_in_block = !paged || log2_bs >= kLog2BK;
+  auto tile_base = [&](int t, const uint16_t* base, int64_t stride) {
+    if (!paged) return base + (kv0 + int64_t(t) * kBK) * stride;
     const int phys = __builtin_amdgcn_readfirstlane(s_ids[t % 3][0]);
-    return base + ((int64_t(phys) << log2_bs) + ((t * kBK) & bs_mask)) * row_elems;
+    return base + ((int64_t(phys) << log2_bs) + ((t * kBK) & bs_mask)) * stride;
   };
   auto issue_k = [&](int t) {
     uint8_t* sk = smem + (t % kStages) * Geo::STAGE;
     const int rmax = lk - 1 - t * kBK;               // rows past the keys repeat the last
     if (tile_in_block) {
-      const uint16_t* tb = tile_base(t, kbase);
+      const uint16_t* tb = tile_base(t, kbase, k_stride);
 #pragma unroll
       for (int j = 0; j < Geo::K_DMA; ++j)
-        load_lds16(tb + min(k_row[j], rmax) * row_elems + k_elem[j],
+        load_lds16(tb + min(k_row[j], rmax) * k_stride + k_elem[j],
                    sk + (wave * Geo::K_DMA + j) * 1024);
     } else {
 #pragma unroll
@@ -193,12 +199,12 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   u32x4_t vreg[KPI];
   auto load_v = [&](int t) {
     if (tile_in_block) {
-      const uint16_t* tb = tile_base(t, vbase) + v_c * 8;
+      const uint16_t* tb = tile_base(t, vbase, v_stride) + v_c * 8;
 #pragma unroll
       for (int j = 0; j < KPI; ++j) {
         const int r = KPI * v_kg + j;
         vreg[j] = (v_item && t * kBK + r < lk)        // rows past the keys are zero, not NaN
-                      ? *reinterpret_cast<const u32x4_t*>(tb + r * row_elems)
+                      ? *reinterpret_cast<const u32x4_t*>(tb + r * v_stride)
                       : u32x4_t{0, 0, 0, 0};
       }
     } else {
@@ -412,6 +418,7 @@ template <int D>
 __global__ void __launch_bounds__(64)
 prefill_f32_kernel(const float* __restrict__ q, int64_t q_row,
                    const float* __restrict__ k_cache, const float* __restrict__ v_cache,
+                   int64_t k_stride, int64_t v_stride,
                    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                    const int32_t* __restrict__ block_table, int32_t max_blocks,
                    int32_t num_q_heads, int32_t num_kv_heads, int32_t log2_bs,
@@ -425,9 +432,10 @@ prefill_f32_kernel(const float* __restrict__ q, int64_t q_row,
   if (qi >= lq) return;
   const int g = h / (num_q_heads / num_kv_heads);
   const int limit = lk - lq + qi;                     // last visible key
-  const int32_t* trow = block_table + int64_t(b) * max_blocks;
+  const bool paged = block_table != nullptr;
+  const int64_t kv0 = paged ? 0 : cu_k[b];
+  const int32_t* trow = paged ? block_table + int64_t(b) * max_blocks : nullptr;
   const int bs_mask = (1 << log2_bs) - 1;
-  const int64_t row_elems = int64_t(num_kv_heads) * D;
 
   float qv[D], acc[D];
   const float* qp = q + int64_t(qstart + qi) * q_row + int64_t(h) * D;
@@ -438,10 +446,9 @@ prefill_f32_kernel(const float* __restrict__ q, int64_t q_row,
   }
   float m = -INFINITY, l = 0.f;
   for (int j = 0; j <= limit; ++j) {
-    const int64_t off = ((int64_t(trow[j >> log2_bs]) << log2_bs) + (j & bs_mask)) * row_elems +
-                        int64_t(g) * D;
-    const float* kp = k_cache + off;
-    const float* vp = v_cache + off;
+    const int64_t row = paged ? (int64_t(trow[j >> log2_bs]) << log2_bs) + (j & bs_mask) : kv0 + j;
+    const float* kp = k_cache + row * k_stride + int64_t(g) * D;
+    const float* vp = v_cache + row * v_stride + int64_t(g) * D;
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; ++d) s = fmaf(qv[d], kp[d], s);
@@ -471,7 +478,7 @@ static hipError_t launch_bf16(const PrefillArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((prefill_bf16_kernel<D, G, QB>), dim3(p.num_seqs * p.num_kv_heads, qtiles),
                      dim3(Geo::NT), 0, st, static_cast<const uint16_t*>(a.q), a.q_row_elems,
                      static_cast<const uint16_t*>(p.k_cache), static_cast<const uint16_t*>(p.v_cache),
-                     a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,
+                     a.k_row_elems, a.v_row_elems, a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,
                      p.num_kv_heads, p.log2_block_size, p.scale_log2e,
                      static_cast<uint16_t*>(a.out));
   return hipGetLastError();
@@ -484,7 +491,7 @@ static hipError_t launch_f32(const PrefillArgs& a, hipStream_t st) {
                      dim3((a.max_seqlen_q + 63) / 64, p.num_q_heads, p.num_seqs), dim3(64), 0, st,
                      static_cast<const float*>(a.q), a.q_row_elems,
                      static_cast<const float*>(p.k_cache), static_cast<const float*>(p.v_cache),
-                     a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,
+                     a.k_row_elems, a.v_row_elems, a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,
                      p.num_q_heads, p.num_kv_heads, p.log2_block_size, p.scale_log2e,
                      static_cast<float*>(a.out));
   return hipGetLastError();

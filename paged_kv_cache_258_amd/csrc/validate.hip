@@ -80,19 +80,21 @@ __device__ __forceinline__ void check_blocks(const int32_t* __restrict__ row, in
 __global__ void __launch_bounds__(64)
 validate_prefill_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                         const int32_t* __restrict__ block_table, int32_t max_blocks,
-                        int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                        int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_seqlen_q,
                         int32_t max_seqlen_k, int32_t log2_bs, int32_t num_blocks) {
   const int b = blockIdx.x * 64 + threadIdx.x;
   if (b >= num_seqs) return;
   if (b == 0 && (cu_q[0] != 0 || cu_k[0] != 0)) report(kValidateSeqlens, 0);
   if (b == num_seqs - 1 && cu_q[num_seqs] != total_q) report(kValidateSeqlens, b);
+  // contiguous K/V (no block table): the keys must lie in the total_k rows given
+  if (total_k >= 0 && b == num_seqs - 1 && cu_k[num_seqs] > total_k) report(kValidateSeqlens, b);
   const int32_t lq = cu_q[b + 1] - cu_q[b];
   const int32_t lk = cu_k[b + 1] - cu_k[b];
   if (lq < 0 || lk < 0 || lq > lk || lq > max_seqlen_q || lk > max_seqlen_k) {
     report(kValidateSeqlens, b);
     return;
   }
-  check_blocks(block_table + int64_t(b) * max_blocks, lk, log2_bs, num_blocks, b);
+  if (block_table) check_blocks(block_table + int64_t(b) * max_blocks, lk, log2_bs, num_blocks, b);
 }
 
 __global__ void __launch_bounds__(64)
@@ -154,15 +156,15 @@ hipError_t validate_rope_store(const int32_t* positions, const int32_t* slots, i
   return collect(st, r);
 }
 
-hipError_t validate_prefill(const PrefillArgs& a, int32_t total_q, int32_t num_blocks,
-                            hipStream_t st, ValidateResult* r) {
+hipError_t validate_prefill(const PrefillArgs& a, int32_t total_q, int32_t total_k,
+                            int32_t num_blocks, hipStream_t st, ValidateResult* r) {
   const PagedArgs& p = a.p;
   hipLaunchKernelGGL(validate_reset_kernel, dim3(1), dim3(64), 0, st);
   if (p.num_seqs > 0)
     hipLaunchKernelGGL(validate_prefill_kernel, dim3((p.num_seqs + 63) / 64), dim3(64), 0, st,
                        a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,
-                       p.num_seqs, total_q, a.max_seqlen_q, a.max_seqlen_k, p.log2_block_size,
-                       num_blocks);
+                       p.num_seqs, total_q, total_k, a.max_seqlen_q, a.max_seqlen_k,
+                       p.log2_block_size, num_blocks);
   return collect(st, r);
 }
 

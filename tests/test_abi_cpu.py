@@ -230,3 +230,38 @@ def test_add_rms_norm_rejects(lib, kw, status):
 
 def test_add_rms_norm_zero_tokens_is_noop(lib):
     assert add_rms(lib, n=0, x=None, r=None, w=None, out=None, ro=None) == _lib.NKV_OK
+
+
+def varlen(lib, **kw):
+    a = dict(q=FAKE, qs=4096, k=FAKE, ks=1024, v=FAKE, vs=1024, cuq=FAKE, cuk=FAKE, b=2, tq=64,
+             tk=64, mq=32, mk=32, hq=32, hkv=8, d=128, scale=0.088, dtype=1, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.nkv_attn_varlen_prefill(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["cuq"],
+                                       a["cuk"], a["b"], a["tq"], a["tk"], a["mq"], a["mk"], a["hq"],
+                                       a["hkv"], a["d"], a["scale"], a["dtype"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), _lib.NKV_ERR_INVALID_ARG),
+    (dict(hq=12), _lib.NKV_ERR_INVALID_ARG),             # 12 heads over 8 KV heads
+    (dict(hq=24, hkv=2), _lib.NKV_ERR_UNSUPPORTED),      # group 12
+    (dict(d=80), _lib.NKV_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), _lib.NKV_ERR_INVALID_ARG),
+    (dict(mq=64, mk=32), _lib.NKV_ERR_INVALID_ARG),      # max_seqlen_q > max_seqlen_k
+    (dict(mk=65), _lib.NKV_ERR_INVALID_ARG),             # max_seqlen_k > total_k
+    (dict(qs=4000), _lib.NKV_ERR_INVALID_ARG),           # below Hq * D
+    (dict(ks=1000), _lib.NKV_ERR_INVALID_ARG),           # below Hkv * D
+    (dict(vs=1028), _lib.NKV_ERR_INVALID_ARG),           # not a multiple of 16 bytes
+    (dict(k=None), _lib.NKV_ERR_INVALID_ARG),
+    (dict(cuk=None), _lib.NKV_ERR_INVALID_ARG),
+    (dict(v=FAKE + 8), _lib.NKV_ERR_INVALID_ARG),
+    (dict(tk=-1), _lib.NKV_ERR_INVALID_ARG),
+])
+def test_varlen_prefill_rejects(lib, kw, status):
+    assert varlen(lib, **kw) == status
+    assert lib.nkv_last_error() != b""
+
+
+def test_varlen_prefill_empty_is_noop(lib):
+    assert varlen(lib, b=0, q=None, k=None, v=None, out=None) == _lib.NKV_OK
+    assert varlen(lib, tq=0, mq=0, q=None) == _lib.NKV_OK
