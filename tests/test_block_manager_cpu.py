@@ -1,0 +1,179 @@
+"""The block manager oracle (oracle/block_manager.py) against what the pages and the hash's
+published definition fix, and the C++ block manager of libnkv.so against the oracle.
+
+Pins: the published FNV-1a vectors (tests/golden/fnv1a64_vectors.json); a hand-worked trace
+(prefix sharing of full blocks, at least one token left to compute, the latest hashed
+block wins, revival of a freed block, reverse-order release, an allocation that does not
+fit); the slot formula of 「同一个 Qwen3，两种写法」 §3.3 (block * block_size + offset);
+invariants on random traces (each block's reference count is the number of live
+block tables holding it, free blocks are exactly those with count 0, equal full-block
+prefixes share physical blocks).  The C++ implementation (the nkv_bm_* calls, host code
+only) must give the same outputs as the oracle, bit for bit, after every operation of
+seeded random traces.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import block_manager as obm
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def test_fnv1a64_published_vectors():
+    g = json.load(open(os.path.join(HERE, "golden", "fnv1a64_vectors.json")))
+    for v in g["vectors"]:
+        assert obm.fnv1a64(v["ascii"].encode()) == int(v["fnv1a64"], 16)
+
+
+def test_block_hash_chains_the_prefix():
+    h0 = obm.block_hash(None, [1, 2, 3, 4])
+    assert h0 == obm.fnv1a64(bytes([1, 0, 0, 0, 2, 0, 0, 0, 3, 0, 0, 0, 4, 0, 0, 0]))
+    h1 = obm.block_hash(h0, [5, 6, 7, 8])
+    assert h1 == obm.fnv1a64(h0.to_bytes(8, "little") + bytes([5, 0, 0, 0, 6, 0, 0, 0, 7, 0, 0, 0, 8, 0, 0, 0]))
+    assert obm.block_hash(None, [5, 6, 7, 8]) != h1          # same tokens, other prefix
+    assert obm.block_hash(None, [-1]) == obm.fnv1a64(b"\xff\xff\xff\xff")
+
+
+def test_hand_worked_trace():
+    bm = obm.BlockManagerRef(8, 4)
+    a, b, c = list(range(1, 11)), list(range(1, 9)) + [11], list(range(1, 9))
+    assert bm.add_sequence("A", a) == 0
+    assert bm.seqs["A"]["table"] == [0, 1, 2] and bm.free == [3, 4, 5, 6, 7]
+    assert bm.add_sequence("B", b) == 8                      # two full blocks shared
+    assert bm.seqs["B"]["table"] == [0, 1, 3] and bm.free == [4, 5, 6, 7]
+    assert [bm.blocks[i].ref for i in (0, 1, 2, 3)] == [2, 2, 1, 1]
+    assert bm.add_sequence("C", c) == 4                      # all hit: the last is recomputed
+    assert bm.seqs["C"]["table"] == [0, 4] and bm.free == [5, 6, 7]
+    h1 = obm.block_hash(obm.block_hash(None, [1, 2, 3, 4]), [5, 6, 7, 8])
+    assert bm.by_hash[h1] == 4                               # the latest hashed block wins
+    p = bm.prepare_prefill(["A", "B", "C"], 3)
+    assert p["cu_seqlens_q"] == [0, 10, 11, 15] and p["cu_seqlens_k"] == [0, 10, 19, 27]
+    assert p["positions"] == list(range(10)) + [8] + [4, 5, 6, 7]
+    assert p["slot_mapping"] == list(range(10)) + [12] + [16, 17, 18, 19]
+    assert p["block_table"] == [[0, 1, 2], [0, 1, 3], [0, 4, -1]]
+    bm.append_token("A", 42)
+    bm.append_token("A", 43)                                 # block 2 full: hashed now
+    assert bm.blocks[1].hash == h1 and bm.blocks[2].hash == obm.block_hash(h1, [9, 10, 42, 43])
+    bm.append_token("A", 44)                                 # a new block from the front
+    assert bm.seqs["A"]["table"] == [0, 1, 2, 5] and bm.free == [6, 7]
+    d = bm.prepare_decode(["A", "B"], 4)
+    assert d == dict(positions=[12, 8], slot_mapping=[20, 12], context_lens=[13, 9],
+                     block_table=[[0, 1, 2, 5], [0, 1, 3, -1]])
+    bm.free_sequence("C")                                    # block 4 freed, its hash kept
+    assert bm.free == [6, 7, 4] and bm.blocks[0].ref == 2
+    assert bm.add_sequence("F", list(range(1, 10))) == 8     # revives block 4
+    assert bm.seqs["F"]["table"] == [0, 4, 6] and bm.free == [7]
+    bm.free_sequence("B")                                    # reverse order: 3 first
+    assert bm.free == [7, 3] and bm.blocks[1].ref == 1 and bm.blocks[0].ref == 2
+    with pytest.raises(obm.NoSpace):
+        bm.add_sequence("G", list(range(100, 112)))          # 3 blocks, 2 free
+    assert bm.free == [7, 3] and "G" not in bm.seqs
+
+
+def check_invariants(bm):
+    counts = np.zeros(len(bm.blocks), dtype=int)
+    for s in bm.seqs.values():
+        assert len(s["table"]) == -(-len(s["tokens"]) // bm.bs)
+        for b in s["table"]:
+            counts[b] += 1
+        # the slot formula and its one-to-one map inside a sequence
+        sl = [s["table"][p // bm.bs] * bm.bs + p % bm.bs for p in range(len(s["tokens"]))]
+        assert len(set(sl)) == len(sl)
+        # every full block that is hashed holds this sequence's tokens and the chained hash
+        prev = None
+        for i in range(len(s["tokens"]) // bm.bs):
+            blk = bm.blocks[s["table"][i]]
+            h = obm.block_hash(prev, s["tokens"][i * bm.bs:(i + 1) * bm.bs])
+            if blk.hash is not None:
+                assert blk.hash == h and blk.tokens == s["tokens"][i * bm.bs:(i + 1) * bm.bs]
+            prev = h
+    assert [blk.ref for blk in bm.blocks] == counts.tolist()
+    assert sorted(bm.free) == [i for i in range(len(bm.blocks)) if counts[i] == 0]
+    assert len(set(bm.free)) == len(bm.free)
+    for h, b in bm.by_hash.items():
+        assert bm.blocks[b].hash == h
+
+
+def random_trace(seed, bm_factory, steps=300, nb=64, bs=4):
+    """Apply one seeded random trace to each manager; yields the outputs after each op."""
+    rng = np.random.default_rng(seed)
+    prefixes = [list(rng.integers(0, 50, size=int(rng.integers(1, 14)))) for _ in range(4)]
+    mgrs = bm_factory(nb, bs)
+    live, next_id = [], 0
+    for step in range(steps):
+        op = rng.integers(0, 10)
+        if op < 4 or not live:
+            base = prefixes[int(rng.integers(0, 4))] if rng.random() < 0.7 else []
+            toks = base + list(rng.integers(0, 50, size=int(rng.integers(1 if not base else 0, 12))))
+            if not toks:
+                toks = [int(rng.integers(0, 50))]
+            sid = next_id
+            next_id += 1
+            outs = [m.add(sid, toks) for m in mgrs]
+            if outs[0] is not None:
+                live.append(sid)
+            yield ("add", sid, outs, mgrs)
+        elif op < 8:
+            sid = live[int(rng.integers(0, len(live)))]
+            tok = int(rng.integers(0, 50))
+            yield ("append", sid, [m.append(sid, tok) for m in mgrs], mgrs)
+        else:
+            sid = live.pop(int(rng.integers(0, len(live))))
+            yield ("free", sid, [m.free(sid) for m in mgrs], mgrs)
+        if live and step % 7 == 0:
+            ids = [live[i] for i in rng.permutation(len(live))[:5]]
+            yield ("prefill", ids, [m.prefill(ids) for m in mgrs], mgrs)
+            yield ("decode", ids, [m.decode(ids) for m in mgrs], mgrs)
+
+
+class OracleSide:
+    """Uniform calls over the oracle: None for a failed admission (no space)."""
+
+    def __init__(self, nb, bs):
+        self.bm = obm.BlockManagerRef(nb, bs)
+        self.maxb = 32
+
+    def add(self, sid, toks):
+        try:
+            return self.bm.add_sequence(sid, toks)
+        except obm.NoSpace:
+            return None
+
+    def append(self, sid, tok):
+        try:
+            self.bm.append_token(sid, tok)
+            return ("ok", self.bm.num_free())
+        except obm.NoSpace:
+            return ("nospace", self.bm.num_free())
+
+    def free(self, sid):
+        self.bm.free_sequence(sid)
+        return self.bm.num_free()
+
+    def prefill(self, ids):
+        return self.bm.prepare_prefill(ids, self.maxb)
+
+    def decode(self, ids):
+        return self.bm.prepare_decode(ids, self.maxb)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_random_traces_keep_the_invariants(seed):
+    for op, sid, outs, mgrs in random_trace(seed, lambda nb, bs: [OracleSide(nb, bs)]):
+        check_invariants(mgrs[0].bm)
+
+
+def test_equal_prefixes_share_physical_blocks():
+    bm = obm.BlockManagerRef(32, 4)
+    sysp = list(range(7, 19))                                # a 12-token "system prompt"
+    for i in range(5):
+        bm.add_sequence(i, sysp + [100 + i, 200 + i])
+    tables = [bm.seqs[i]["table"] for i in range(5)]
+    assert all(t[:3] == tables[0][:3] for t in tables)       # the 3 full prefix blocks, once
+    assert len({t[3] for t in tables}) == 5
+    assert [bm.blocks[b].ref for b in tables[0][:3]] == [5, 5, 5]
+    assert bm.num_free() == 32 - 3 - 5
