@@ -34,6 +34,9 @@ qk_norm_rope_store = the fused q/k RMSNorm + rotary + KV store over C3's 16384 p
 tokens and C2's 64 decode tokens: algorithmic bytes / mean event time vs 8 TB/s.
 add_rms_norm = the fused residual add + RMSNorm over the same token counts' 4096-wide
 hidden rows (the norm in front of each block's projections), same figures.
+block_manager = host wall time of the C++ block manager (through the binding): admitting
+the long-context batch's 256 prompts and building one decode step's and one 8 x 2048
+prefill's index arrays.
 prefill also holds the varlen leg: C3's prompts through the prefill over contiguous K/V
 (views of a packed qkv, the branch without a prefix cache), timed like the paged legs.
 
@@ -326,6 +329,61 @@ def bench_varlen_prefill(dev, steps, warmup, settle_s=0.25):
     return {"workload": "C3 prompts, contiguous K/V views of a packed qkv", "prefill_us": st["median_us"],
             "tflops": round(tflops, 2), "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "flop": flops, "prefill_call": st, "cold_prefill_call": cold, "settle_s": settle_s}
+
+
+def bench_block_manager(reps=20):
+    """Host cost of the C++ block manager on the long-context batch's shape: admit C5b's
+    256 prompts (lengths log-uniform in [128, 32768], block_size 256; the first 64 share a
+    4096-token prefix), then build the index arrays of one decode step for all 256 (one
+    appended token each) and of a C3-shaped prefill (8 x 2048).  Median wall time per call."""
+    import numpy as np
+    import paged_kv_cache_258_amd as nkv
+    from paged_kv_cache_258_amd import workloads as wl
+
+    lens, _ = wl.c5_lengths("b", wl.SEED_BASE + 6)
+    rng = np.random.default_rng(wl.SEED_BASE + 80)
+    bs = 256
+    shared = rng.integers(0, 151936, size=4096).astype(np.int32)
+    prompts = []
+    for i, n in enumerate(lens):
+        t = rng.integers(0, 151936, size=int(n)).astype(np.int32)
+        if i < 64 and n > 4096:
+            t[:4096] = shared
+        prompts.append(t)
+    nblocks = sum(-(-int(n) // bs) + 1 for n in lens)
+    maxb = max(-(-int(n) // bs) for n in lens) + 1
+
+    def med(xs):
+        return round(1e6 * sorted(xs)[len(xs) // 2], 1)
+
+    admit, dec, cached = [], [], 0
+    for r in range(max(3, reps // 4)):
+        bm = nkv.BlockManager(nblocks, bs)
+        t0 = time.perf_counter()
+        cached = sum(bm.add_sequence(i, p) for i, p in enumerate(prompts))
+        admit.append(time.perf_counter() - t0)
+    ids = list(range(len(prompts)))
+    for i in ids:
+        bm.append_token(i, 7)
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        bm.prepare_decode(ids, maxb)
+        dec.append(time.perf_counter() - t0)
+    bm3 = nkv.BlockManager(8 * 8, bs)
+    for i in range(8):
+        bm3.add_sequence(i, rng.integers(0, 151936, size=2048).astype(np.int32))
+    pre = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        bm3.prepare_prefill(list(range(8)), 8)
+        pre.append(time.perf_counter() - t0)
+    out = {"admit_256_prompts_us": med(admit), "prompt_tokens": int(sum(lens)), "cached_tokens": int(cached),
+           "prepare_decode_256_us": med(dec), "prepare_prefill_8x2048_us": med(pre),
+           "note": "host wall time through the Python binding, median"}
+    log(f"[block manager] admit 256 prompts ({int(sum(lens))} tokens, {int(cached)} cached) "
+        f"{out['admit_256_prompts_us']:.0f} us; decode arrays {out['prepare_decode_256_us']:.0f} us; "
+        f"prefill arrays (8 x 2048) {out['prepare_prefill_8x2048_us']:.0f} us")
+    return out
 
 
 def bench_rope_store(dev, which, steps, warmup):
@@ -657,6 +715,7 @@ def main():
         for kind in ("a", "b"):
             long_decode.append(bench_c5(dev, kind, 5, 1))
     cpu = None if args.no_cpu else cpu_baseline(d["case"])
+    block_manager = bench_block_manager()
 
     step_bytes = d["dec_bytes"] + d["st_bytes"]
     value = step_bytes / d["graph_ms_step"] / 1e6
@@ -709,6 +768,7 @@ def main():
         "qk_norm_rope_store": rope_store,
         "add_rms_norm": add_rms,
         "long_decode": long_decode,
+        "block_manager": block_manager,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -83,7 +83,8 @@ typedef enum {
   NKV_ERR_INVALID_ARG = 1, /* a host-checkable argument is wrong                  */
   NKV_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels are built for    */
   NKV_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required    */
-  NKV_ERR_HIP = 4          /* the HIP runtime reported an error                     */
+  NKV_ERR_HIP = 4,         /* the HIP runtime reported an error                     */
+  NKV_ERR_NO_SPACE = 5     /* block manager: not enough free blocks (nothing changed) */
 } nkv_status_t;
 
 typedef enum {
@@ -297,6 +298,77 @@ nkv_status_t nkv_paged_attn_decode(const void* q,
                                    float softmax_scale, nkv_dtype_t dtype,
                                    void* out, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * ---- The CPU block manager (host memory and host code only; no device calls) ----
+ *
+ * The control plane that feeds the calls above: it hands out the blocks of a pool of
+ * num_blocks blocks of block_size slots, keeps a reference count per block, shares the
+ * full blocks of equal prompt prefixes between sequences, and writes the index arrays
+ * the data plane reads.  「Nano-vLLM深度解读（下）」 §4 (the CPU block manager: token
+ * blocks with a hash and a reference count, block ids, prefix-cache reuse, the slot
+ * mapping it provides); 「同一个 Qwen3，两种写法」 §3.3 (fixed-size blocks, block table
+ * logical -> physical, slot = block * block_size + offset, equal prefixes sharing a
+ * physical block by reference count and prefix hash).
+ *
+ * Rules where the pages stop: a full block's hash is 64-bit FNV-1a over the previous
+ * block's hash (8 bytes little-endian, none for the first block) and its token ids (4
+ * bytes each, little-endian), and a hit also compares the token ids; a new sequence
+ * reuses its leading full blocks while they hit and always leaves at least one token to
+ * compute; free blocks are a FIFO queue in which a released block keeps its hash (a later
+ * prefix can revive it) until it is taken for new content; a newly hashed block becomes
+ * the entry for its hash; a sequence's blocks are released in reverse order.  An
+ * operation that needs more free blocks than there are returns NKV_ERR_NO_SPACE and
+ * changes nothing.  Arrays are HOST arrays owned by the caller; a manager is not
+ * thread-safe.  Errors set nkv_last_error() like every other call.
+ */
+typedef struct nkv_block_manager nkv_block_manager_t;
+
+/* A manager over num_blocks blocks of block_size slots, all free (block ids 0..). */
+nkv_status_t nkv_bm_create(int32_t num_blocks, int32_t block_size, nkv_block_manager_t** out);
+void nkv_bm_destroy(nkv_block_manager_t* bm);
+/* Number of free blocks (-1 for a null manager). */
+int32_t nkv_bm_num_free_blocks(const nkv_block_manager_t* bm);
+
+/* Admit sequence seq_id with its prompt token_ids[num_tokens] (num_tokens >= 1): reuse
+ * the leading cached full blocks, take free blocks for the rest.  *num_cached_tokens
+ * (may be NULL) receives the number of prompt tokens whose K/V is already in the pool. */
+nkv_status_t nkv_bm_add_sequence(nkv_block_manager_t* bm, int64_t seq_id, const int32_t* token_ids,
+                                 int32_t num_tokens, int32_t* num_cached_tokens);
+/* Append one generated token (a new block when the last one is full; a block that
+ * becomes full is hashed). */
+nkv_status_t nkv_bm_append_token(nkv_block_manager_t* bm, int64_t seq_id, int32_t token_id);
+/* Release a finished sequence's blocks. */
+nkv_status_t nkv_bm_free_sequence(nkv_block_manager_t* bm, int64_t seq_id);
+
+/* Index arrays of a prefill batch (the sequences' uncached prompt tokens as queries, all
+ * their tokens as keys), for nkv_qk_norm_rope_store / nkv_store_kvcache and
+ * nkv_paged_attn_prefill:
+ *   cu_seqlens_q, cu_seqlens_k  [num_seqs + 1];
+ *   positions, slot_mapping     [total_q], capacity = their length (if it is too small
+ *                               the call fails and *total_q still gives the need);
+ *   block_table                 [num_seqs, max_blocks_per_seq], -1 past each sequence's
+ *                               blocks;
+ *   total_q, max_seqlen_q, max_seqlen_k  outputs (may be NULL). */
+nkv_status_t nkv_bm_prepare_prefill(const nkv_block_manager_t* bm, const int64_t* seq_ids, int32_t num_seqs,
+                                    int32_t max_blocks_per_seq, int32_t capacity, int32_t* cu_seqlens_q,
+                                    int32_t* cu_seqlens_k, int32_t* positions, int32_t* slot_mapping,
+                                    int32_t* block_table, int32_t* total_q, int32_t* max_seqlen_q,
+                                    int32_t* max_seqlen_k);
+/* Index arrays of a decode step (each sequence's last token as the query):
+ *   positions, slot_mapping, context_lens [num_seqs]; block_table as above. */
+nkv_status_t nkv_bm_prepare_decode(const nkv_block_manager_t* bm, const int64_t* seq_ids, int32_t num_seqs,
+                                   int32_t max_blocks_per_seq, int32_t* positions, int32_t* slot_mapping,
+                                   int32_t* context_lens, int32_t* block_table);
+
+/* Inspection (tests, debugging): a sequence's sizes; a block's reference count, hash
+ * and whether it is free; the free queue front to back (returns its length, writes at
+ * most capacity ids). */
+nkv_status_t nkv_bm_sequence_info(const nkv_block_manager_t* bm, int64_t seq_id, int32_t* num_tokens,
+                                  int32_t* num_cached_tokens, int32_t* num_blocks);
+nkv_status_t nkv_bm_block_info(const nkv_block_manager_t* bm, int32_t block_id, int32_t* ref_count,
+                               int32_t* is_hashed, uint64_t* hash, int32_t* is_free);
+int32_t nkv_bm_free_queue(const nkv_block_manager_t* bm, int32_t* out, int32_t capacity);
 
 #ifdef __cplusplus
 } /* extern "C" */

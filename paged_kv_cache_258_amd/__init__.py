@@ -3,6 +3,9 @@ contiguous K/V for the no-prefix-cache branch, and the fused
 q/k norm + rotary + store before them, the residual add + RMSNorm in front of each
 block's projections) for MI355X.
 
+``BlockManager`` drives the library's CPU block manager (block allocation, reference
+counts, prefix sharing) that writes the index arrays those calls read.
+
 The compute lives in ``libnkv.so`` (HIP kernels for gfx950 behind the C ABI of
 ``include/nkv.h``); this package is its thin Python binding plus the seeded input
 generators (``workloads``) and the algorithmic byte/flop accounting (``accounting``).
@@ -10,6 +13,7 @@ The library is loaded on first use and the calls raise if it is not built.
 """
 
 from ._lib import (  # noqa: F401
+    BlockManager,
     NkvError,
     load,
     nkv_add_rms_norm,
@@ -22,6 +26,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
+    "BlockManager",
     "NkvError",
     "load",
     "nkv_store_kvcache",

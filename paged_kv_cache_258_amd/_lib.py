@@ -16,7 +16,7 @@ import torch
 LIB_PATH = os.environ.get("NKV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                      "libnkv.so")
 
-NKV_OK, NKV_ERR_INVALID_ARG, NKV_ERR_UNSUPPORTED, NKV_ERR_WORKSPACE, NKV_ERR_HIP = range(5)
+NKV_OK, NKV_ERR_INVALID_ARG, NKV_ERR_UNSUPPORTED, NKV_ERR_WORKSPACE, NKV_ERR_HIP, NKV_ERR_NO_SPACE = range(6)
 NKV_F32, NKV_BF16 = 0, 1
 ABI_VERSION = 1
 
@@ -31,6 +31,17 @@ EXPORTS = (
     "nkv_attn_varlen_prefill",
     "nkv_paged_attn_decode_workspace_size",
     "nkv_paged_attn_decode",
+    "nkv_bm_create",
+    "nkv_bm_destroy",
+    "nkv_bm_num_free_blocks",
+    "nkv_bm_add_sequence",
+    "nkv_bm_append_token",
+    "nkv_bm_free_sequence",
+    "nkv_bm_prepare_prefill",
+    "nkv_bm_prepare_decode",
+    "nkv_bm_sequence_info",
+    "nkv_bm_block_info",
+    "nkv_bm_free_queue",
 )
 
 _lib = None
@@ -43,7 +54,7 @@ class NkvError(RuntimeError):
 
 
 _STATUS_NAMES = {0: "NKV_OK", 1: "NKV_ERR_INVALID_ARG", 2: "NKV_ERR_UNSUPPORTED",
-                 3: "NKV_ERR_WORKSPACE", 4: "NKV_ERR_HIP"}
+                 3: "NKV_ERR_WORKSPACE", 4: "NKV_ERR_HIP", 5: "NKV_ERR_NO_SPACE"}
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -84,6 +95,25 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nkv_paged_attn_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32,
                                           c_i32, c_i32, c_i32, c_f, ctypes.c_int, c_p, c_p,
                                           ctypes.c_size_t, c_p]
+    p_i32, p_i64, p_u64 = (ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
+                           ctypes.POINTER(ctypes.c_uint64))
+    pp = ctypes.POINTER(c_p)
+    for name, res, args in (
+            ("nkv_bm_create", ctypes.c_int, [c_i32, c_i32, pp]),
+            ("nkv_bm_destroy", None, [c_p]),
+            ("nkv_bm_num_free_blocks", c_i32, [c_p]),
+            ("nkv_bm_add_sequence", ctypes.c_int, [c_p, c_i64, p_i32, c_i32, p_i32]),
+            ("nkv_bm_append_token", ctypes.c_int, [c_p, c_i64, c_i32]),
+            ("nkv_bm_free_sequence", ctypes.c_int, [c_p, c_i64]),
+            ("nkv_bm_prepare_prefill", ctypes.c_int, [c_p, p_i64, c_i32, c_i32, c_i32, p_i32, p_i32, p_i32,
+                                                      p_i32, p_i32, p_i32, p_i32, p_i32]),
+            ("nkv_bm_prepare_decode", ctypes.c_int, [c_p, p_i64, c_i32, c_i32, p_i32, p_i32, p_i32, p_i32]),
+            ("nkv_bm_sequence_info", ctypes.c_int, [c_p, c_i64, p_i32, p_i32, p_i32]),
+            ("nkv_bm_block_info", ctypes.c_int, [c_p, c_i32, p_i32, p_i32, p_u64, p_i32]),
+            ("nkv_bm_free_queue", c_i32, [c_p, p_i32, c_i32])):
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
     if lib.nkv_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libnkv.so ABI {lib.nkv_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -318,3 +348,103 @@ def nkv_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                                      ws_bytes, _stream(q)),
            "nkv_paged_attn_decode")
     return out
+
+
+# ---------------------------------------------------------------------------------------
+# the CPU block manager (host arrays; the nkv_bm_* calls)
+# ---------------------------------------------------------------------------------------
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class BlockManager:
+    """Handle on a C++ block manager (nkv_bm_*): admits sequences, appends tokens, frees
+    them, and fills the host index arrays of prefill and decode batches."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        import numpy as np  # noqa: F401  (arrays below)
+        lib = load()
+        h = ctypes.c_void_p()
+        _check(lib.nkv_bm_create(num_blocks, block_size, ctypes.byref(h)), "nkv_bm_create")
+        self._h, self.num_blocks, self.block_size = h, num_blocks, block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.nkv_bm_destroy(h)
+            self._h = None
+
+    def num_free_blocks(self) -> int:
+        return int(load().nkv_bm_num_free_blocks(self._h))
+
+    def add_sequence(self, seq_id: int, token_ids) -> int:
+        """Returns the number of prompt tokens already cached; NkvError(NKV_ERR_NO_SPACE) if
+        the free blocks do not suffice (nothing changes then)."""
+        import numpy as np
+        t = np.ascontiguousarray(token_ids, dtype=np.int32)
+        cached = ctypes.c_int32(0)
+        _check(load().nkv_bm_add_sequence(self._h, int(seq_id), _i32p(t), len(t), ctypes.byref(cached)),
+               "nkv_bm_add_sequence")
+        return cached.value
+
+    def append_token(self, seq_id: int, token_id: int) -> None:
+        _check(load().nkv_bm_append_token(self._h, int(seq_id), int(token_id)), "nkv_bm_append_token")
+
+    def free_sequence(self, seq_id: int) -> None:
+        _check(load().nkv_bm_free_sequence(self._h, int(seq_id)), "nkv_bm_free_sequence")
+
+    def sequence_info(self, seq_id: int):
+        n, c, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(load().nkv_bm_sequence_info(self._h, int(seq_id), ctypes.byref(n), ctypes.byref(c),
+                                           ctypes.byref(b)), "nkv_bm_sequence_info")
+        return dict(num_tokens=n.value, num_cached_tokens=c.value, num_blocks=b.value)
+
+    def block_info(self, block_id: int):
+        ref, hashed, free = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        h = ctypes.c_uint64()
+        _check(load().nkv_bm_block_info(self._h, int(block_id), ctypes.byref(ref), ctypes.byref(hashed),
+                                        ctypes.byref(h), ctypes.byref(free)), "nkv_bm_block_info")
+        return dict(ref=ref.value, hash=h.value if hashed.value else None, free=bool(free.value))
+
+    def free_queue(self):
+        import numpy as np
+        n = int(load().nkv_bm_free_queue(self._h, None, 0))
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        load().nkv_bm_free_queue(self._h, _i32p(out), n)
+        return out[:n].tolist()
+
+    def prepare_prefill(self, seq_ids, max_blocks_per_seq: int):
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        b = len(ids)
+        cu_q, cu_k = np.zeros(b + 1, np.int32), np.zeros(b + 1, np.int32)
+        table = np.zeros((max(b, 1), max_blocks_per_seq), np.int32)
+        tq, mq, mk = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        lib = load()
+        ids_p = ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        need = 0
+        for _ in range(2):                 # size the token arrays, then fill them
+            pos, slots = np.zeros(max(need, 1), np.int32), np.zeros(max(need, 1), np.int32)
+            st = lib.nkv_bm_prepare_prefill(self._h, ids_p, b, max_blocks_per_seq, need, _i32p(cu_q), _i32p(cu_k),
+                                            _i32p(pos), _i32p(slots), _i32p(table), ctypes.byref(tq),
+                                            ctypes.byref(mq), ctypes.byref(mk))
+            if st == NKV_OK:
+                break
+            if tq.value <= need:
+                _check(st, "nkv_bm_prepare_prefill")
+            need = tq.value
+        _check(st, "nkv_bm_prepare_prefill")
+        return dict(cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, positions=pos[:tq.value], slot_mapping=slots[:tq.value],
+                    block_table=table[:b], max_seqlen_q=mq.value, max_seqlen_k=mk.value)
+
+    def prepare_decode(self, seq_ids, max_blocks_per_seq: int):
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        b = len(ids)
+        pos, slots, lens = (np.zeros(max(b, 1), np.int32) for _ in range(3))
+        table = np.zeros((max(b, 1), max_blocks_per_seq), np.int32)
+        _check(load().nkv_bm_prepare_decode(self._h, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), b,
+                                            max_blocks_per_seq, _i32p(pos), _i32p(slots), _i32p(lens),
+                                            _i32p(table)), "nkv_bm_prepare_decode")
+        return dict(positions=pos[:b], slot_mapping=slots[:b], context_lens=lens[:b], block_table=table[:b])

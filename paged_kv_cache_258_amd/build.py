@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnkv.so")
-SOURCES = ["api.hip", "store.hip", "rope_store.hip", "rmsnorm.hip", "decode.hip", "prefill.hip", "validate.hip"]
+SOURCES = ["api.hip", "store.hip", "rope_store.hip", "rmsnorm.hip", "decode.hip", "prefill.hip", "validate.hip",
+           "block_manager.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -43,6 +44,17 @@ SOURCE_FLAGS = {
 }
 
 
+# host-only sources
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-I", os.path.join(ROOT, "include")]
+
+
+def _cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler (g++) found")
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -63,8 +75,11 @@ def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BU
     os.makedirs(build_dir, exist_ok=True)
     objs, cmds = [], []
     for src in SOURCES:
-        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
+        if src.endswith(".cpp"):      # host-only C++ (the block manager)
+            cmds.append([_cxx(), *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+            continue
         cmds.append([hipcc, *FLAGS, *SOURCE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c",
                      os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:

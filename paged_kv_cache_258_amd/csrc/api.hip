@@ -13,6 +13,7 @@
 
 #include "nkv.h"  // include/ is on the include path
 #include "launch.hpp"
+#include "status.hpp"
 
 #define NKV_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -147,6 +148,15 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 }  // namespace
 
+// The calling thread's last error, for the host-only parts of the library (status.hpp).
+namespace nkv {
+nkv_status_t set_error(nkv_status_t st, const char* msg) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+  return st;
+}
+nkv_status_t clear_error() { return ok(); }
+}  // namespace nkv
+
 NKV_EXPORT int nkv_abi_version(void) { return NKV_ABI_VERSION; }
 
 NKV_EXPORT const char* nkv_status_string(nkv_status_t s) {
@@ -156,6 +166,7 @@ NKV_EXPORT const char* nkv_status_string(nkv_status_t s) {
     case NKV_ERR_UNSUPPORTED: return "NKV_ERR_UNSUPPORTED";
     case NKV_ERR_WORKSPACE: return "NKV_ERR_WORKSPACE";
     case NKV_ERR_HIP: return "NKV_ERR_HIP";
+    case NKV_ERR_NO_SPACE: return "NKV_ERR_NO_SPACE";
   }
   return "NKV_UNKNOWN_STATUS";
 }

@@ -101,7 +101,7 @@ def check_invariants(bm):
 def random_trace(seed, bm_factory, steps=300, nb=64, bs=4):
     """Apply one seeded random trace to each manager; yields the outputs after each op."""
     rng = np.random.default_rng(seed)
-    prefixes = [list(rng.integers(0, 50, size=int(rng.integers(1, 14)))) for _ in range(4)]
+    prefixes = [list(rng.integers(0, 50, size=int(rng.integers(1, 3 * bs + 3)))) for _ in range(4)]
     mgrs = bm_factory(nb, bs)
     live, next_id = [], 0
     for step in range(steps):
@@ -177,3 +177,83 @@ def test_equal_prefixes_share_physical_blocks():
     assert len({t[3] for t in tables}) == 5
     assert [bm.blocks[b].ref for b in tables[0][:3]] == [5, 5, 5]
     assert bm.num_free() == 32 - 3 - 5
+
+
+class CppSide:
+    """The same calls on the C++ block manager of libnkv.so (host code only)."""
+
+    def __init__(self, nb, bs):
+        from paged_kv_cache_258_amd import BlockManager
+        self.bm = BlockManager(nb, bs)
+        self.maxb = 32
+
+    def add(self, sid, toks):
+        from paged_kv_cache_258_amd import NkvError, _lib
+        try:
+            return self.bm.add_sequence(sid, toks)
+        except NkvError as e:
+            assert e.status == _lib.NKV_ERR_NO_SPACE
+            return None
+
+    def append(self, sid, tok):
+        from paged_kv_cache_258_amd import NkvError, _lib
+        try:
+            self.bm.append_token(sid, tok)
+            return ("ok", self.bm.num_free_blocks())
+        except NkvError as e:
+            assert e.status == _lib.NKV_ERR_NO_SPACE
+            return ("nospace", self.bm.num_free_blocks())
+
+    def free(self, sid):
+        self.bm.free_sequence(sid)
+        return self.bm.num_free_blocks()
+
+    def prefill(self, ids):
+        p = self.bm.prepare_prefill(ids, self.maxb)
+        return dict(cu_seqlens_q=p["cu_seqlens_q"].tolist(), cu_seqlens_k=p["cu_seqlens_k"].tolist(),
+                    positions=p["positions"].tolist(), slot_mapping=p["slot_mapping"].tolist(),
+                    block_table=p["block_table"].tolist())
+
+    def decode(self, ids):
+        return {k: v.tolist() for k, v in self.bm.prepare_decode(ids, self.maxb).items()}
+
+
+@pytest.mark.parametrize("seed,nb,bs", [(11, 64, 4), (12, 40, 4), (13, 200, 16), (14, 24, 2), (15, 64, 1)])
+def test_cpp_block_manager_matches_oracle(seed, nb, bs):
+    both = lambda n, b: [OracleSide(n, b), CppSide(n, b)]
+    steps = 0
+    for op, sid, outs, mgrs in random_trace(seed, lambda _n, _b: both(nb, bs), steps=400, nb=nb, bs=bs):
+        assert outs[0] == outs[1], (op, sid, outs)
+        ref, cpp = mgrs[0].bm, mgrs[1].bm
+        assert cpp.free_queue() == ref.free
+        for b in range(nb):
+            info = cpp.block_info(b)
+            assert info["ref"] == ref.blocks[b].ref
+            assert info["free"] == (b in ref.free)
+            if ref.blocks[b].ref > 0 or b in ref.free:
+                assert info["hash"] == ref.blocks[b].hash, (op, b)
+        steps += 1
+    assert steps > 400
+
+
+def test_cpp_block_manager_rejects():
+    from paged_kv_cache_258_amd import BlockManager, NkvError, _lib
+    with pytest.raises(NkvError):
+        BlockManager(0, 16)
+    bm = BlockManager(4, 16)
+    with pytest.raises(NkvError):
+        bm.add_sequence(1, [])
+    bm.add_sequence(1, [1, 2, 3])
+    with pytest.raises(NkvError) as e:
+        bm.add_sequence(1, [4])                              # the id is taken
+    assert e.value.status == _lib.NKV_ERR_INVALID_ARG
+    with pytest.raises(NkvError) as e:
+        bm.add_sequence(2, list(range(64)))                  # 4 blocks, 3 free
+    assert e.value.status == _lib.NKV_ERR_NO_SPACE
+    assert bm.num_free_blocks() == 3 and bm.free_queue() == [1, 2, 3]
+    with pytest.raises(NkvError):
+        bm.append_token(9, 1)
+    with pytest.raises(NkvError):
+        bm.prepare_decode([1, 9], 4)
+    with pytest.raises(NkvError):
+        bm.prepare_prefill([1], 0)
