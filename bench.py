@@ -13,8 +13,9 @@ A step is one pass of the hot path over one batch of synthetic input:
     pools for 4 x 40960 (C5a) and 256 log-uniform lengths in [128, 32768] (C5b).
 
 value = algorithmic bytes of the decode step (store + decode) / measured step time, the
-step replayed from a HIP graph as a serving engine runs decode (one captured graph per
-rotated pool copy; ms_per_step is its event time per step).  eager_step gives the same
+step replayed from HIP graphs as a serving engine runs decode (a graph of three steps,
+one per rotated pool copy, plus single-step graphs for the remainder, so exactly `steps`
+steps are timed; ms_per_step is the event time per step).  eager_step gives the same
 step launched call by call.
 roofline = the decode call (stream-K kernel + its fixup kernel) timed with HIP events on
 the stream it runs on: algorithmic decode bytes / average duration vs 8 TB/s.
@@ -25,9 +26,10 @@ cpu_baseline = the float64 CPU oracle (store_ref + decode_ref) on the same C2 ba
 decode_call / prefill_call / store_call = mean, median and minimum of the per-call event times; the
 prefill legs' headline times (the prefill and the store before it) are the median calls.
 Prefill legs are timed in steady state: after the warm-up calls, 10 calls are timed at once
-(cold_prefill_call), the matrix cores are then kept busy for settle_s seconds (the first
-tens of milliseconds of back-to-back MFMA work run slower while the engine clock
-settles), and only then are the `steps` reported calls timed.
+(cold_prefill_call), the matrix cores are then kept busy for settle_s = 1.5 seconds (the
+first sustained MFMA work of a process runs slower while the engine clock settles: the
+first leg measured 370 us per C3 call after 0.25 s of it and 331 us after 1.5 s), and only
+then are the `steps` reported calls timed.
 peaks = the spec peaks beside CUs x max engine clock x 4096 flop/clock (bf16 MFMA) from the
 device properties.
 qk_norm_rope_store = the fused q/k RMSNorm + rotary + KV store over C3's 16384 prompt
@@ -179,8 +181,8 @@ def bench_decode(dev, steps, warmup, graph=True):
     log(f"[decode C2] step {ms_step*1e3:.1f} us (store {store_ms*1e3:.1f} us, decode "
         f"{dec_ms*1e3:.1f} us) -> decode {dec_bytes/dec_ms/1e6:.0f} GB/s, wall {wall:.3f}s")
 
-    # The same steps replayed from HIP graphs: one step captured per pool copy, after a warm-up
-    # call on a side stream.  The calls allocate, memset and synchronise nothing.
+    # The same steps replayed from HIP graphs, captured after a warm-up call on a side
+    # stream.  The calls allocate, memset and synchronise nothing.
     if not graph:
         return dict(case=case, ms_step=ms_step, store_ms=store_ms, dec_ms=dec_ms, dec_bytes=dec_bytes,
                     st_bytes=st_bytes, workspace_bytes=need, dec_stats=dec_stats, store_stats=store_stats)
@@ -190,16 +192,24 @@ def bench_decode(dev, steps, warmup, graph=True):
         step(0)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = [torch.cuda.CUDAGraph() for _ in range(3)]
-    for i, g in enumerate(graphs):              # one graph per rotated pool copy
+    # one graph of three steps (one per rotated pool copy) for the bulk of the steps, and
+    # one single-step graph per copy for the remainder
+    three = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(three):
+        for i in range(3):
+            step(i)
+    single = [torch.cuda.CUDAGraph() for _ in range(3)]
+    for i, g in enumerate(single):
         with torch.cuda.graph(g):
             step(i)
-    for i in range(warmup):
-        graphs[i % 3].replay()
+    for _ in range(max(1, warmup // 3)):
+        three.replay()
     torch.cuda.synchronize()
     t0.record()
-    for i in range(steps):
-        graphs[i % 3].replay()
+    for _ in range(steps // 3):
+        three.replay()
+    for i in range(steps % 3):
+        single[i].replay()
     t1.record()
     torch.cuda.synchronize()
     graph_ms_step = t0.elapsed_time(t1) / steps
@@ -209,7 +219,7 @@ def bench_decode(dev, steps, warmup, graph=True):
                 graph_ms_step=graph_ms_step)
 
 
-def bench_prefill(dev, which, steps, warmup, settle_s=0.25):
+def bench_prefill(dev, which, steps, warmup, settle_s=1.5):
     import torch
     import paged_kv_cache_258_amd as nkv
     from paged_kv_cache_258_amd import accounting as acc
@@ -279,7 +289,7 @@ def bench_prefill(dev, which, steps, warmup, settle_s=0.25):
             "store_gbs": round(st_bytes / store_ms / 1e6, 1)}
 
 
-def bench_varlen_prefill(dev, steps, warmup, settle_s=0.25):
+def bench_varlen_prefill(dev, steps, warmup, settle_s=1.5):
     """C3's 8 x 2048-token prompts through the prefill over contiguous K/V (the branch
     without a prefix cache): q, k and v are views of one packed N(0,1) projection output
     [16384, (32 + 2*8) * 128] bf16.  Timed like the paged legs (cold calls, settle, median)."""
