@@ -25,7 +25,7 @@
 //   and runs ~1.4x slower), and the four waves of a CU interleave one another's MFMA and
 //   softmax phases anyway.  The softmax uses one
 //   FMA + exp2 per score (scale folded in), the running max is raised lazily (rescale
-//   only past 2^8 headroom), and the row sum is a dot2 of the rounded bf16 weights.
+//   only past 2^8 headroom, detected from the weights' sum), and the row sum is a dot2 of the rounded bf16 weights.
 //   Only tiles that cross the causal diagonal or the end of the keys are masked.  The
 //   output goes through LDS so each row is written as one contiguous run.
 // fp32 path: a plain VALU kernel (one lane per query and head, online softmax), used
@@ -43,21 +43,26 @@ namespace nkv {
 #ifndef NKV_PREFILL_BK
 #define NKV_PREFILL_BK 128
 #endif
+#ifndef NKV_PREFILL_NW
+#define NKV_PREFILL_NW 8
+#endif
 
 constexpr int kBK = NKV_PREFILL_BK;     // keys per tile (a multiple of 32)
 constexpr int kStages = 2;              // K/V tiles in LDS (one computed, one landing)
-constexpr float kLazy = 8.0f;           // log2 headroom before rescaling
+constexpr float kLazyBound = 256.0f;    // largest weight kept before rescaling (2^8 headroom)
 constexpr int kVPad = 8;                // bf16 elements of padding per Vt row in LDS
 constexpr int kMaxIds = kBK / 16;       // block ids per tile (block_size >= 16)
 constexpr int kLog2BK = kBK == 128 ? 7 : 6;
 static_assert(kBK == 64 || kBK == 128, "64- or 128-key tiles");
 
-// QB: 32-query blocks per wave.  QB = 1: eight waves of 32 queries (two per SIMD);
-// QB = 2: four waves of 64 queries (one per SIMD), each K/V fragment read from LDS
-// feeding two MFMAs.
-template <int D, int G, int QB>
+// QB: 32-query blocks per wave.  QB = 1: NKV_PREFILL_NW waves of 32 queries; QB = 2:
+// half as many waves of 64 queries, each K/V fragment read from LDS feeding two MFMAs.
+// Eight waves of 32 queries run two per SIMD inside one workgroup; four waves with
+// 64-key tiles (68 KB of LDS) let two workgroups share a CU, whose barriers, prologues
+// and epilogues are then independent of each other.
+template <int D, int G, int QB, int NWAVES>
 struct PfGeom {
-  static constexpr int NW = 8 / QB;             // waves per workgroup
+  static constexpr int NW = NWAVES;             // waves per workgroup
   static constexpr int NT = NW * kWave;
   static constexpr int WQ = 32 * QB;            // queries per wave
   static constexpr int QSUB = NW / G;           // query sub-tiles per workgroup
@@ -87,8 +92,8 @@ __device__ __forceinline__ int vt_quad_pos(int kq) {
   return (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
 }
 
-template <int D, int G, int QB>
-__global__ void __launch_bounds__(8 / QB * 64)
+template <int D, int G, int QB, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2 / QB)))
 prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                     int64_t k_stride, int64_t v_stride,
@@ -96,7 +101,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     const int32_t* __restrict__ block_table, int32_t max_blocks,
                     int32_t num_kv_heads, int32_t log2_bs, float scale_log2e,
                     uint16_t* __restrict__ out) {
-  using Geo = PfGeom<D, G, QB>;
+  using Geo = PfGeom<D, G, QB, NW>;
   constexpr int KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, VROW = Geo::VROW, WQ = Geo::WQ;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Geo::SMEM];
   __shared__ int32_t s_ids[3][kMaxIds];               // block ids of tiles t, t+1, t+2
@@ -116,7 +121,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = g * G + wave % G;
-  if (wave < 4) __builtin_amdgcn_s_setprio(3);   // waves 0-3 lead their SIMD partners
+  if (NW == 8 && wave < 4) __builtin_amdgcn_s_setprio(3);   // waves 0-3 lead their SIMD partners
   const int hq = G * num_kv_heads;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -280,18 +285,37 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     for (int ks = 1; ks < KS; ++ks)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qb][ks], s, 0, 0, 0);
   };
-  auto pv = [&](const bf16x8_t (&vf)[2][DT], int qb, const bf16x8_t (&pf)[2]) {
+  auto pv = [&](const bf16x8_t (&vf)[2][DT], int qb, int kk, const bf16x8_t& pf) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][dt], pf[kk], o[qb][dt], 0, 0, 0);
+    for (int dt = 0; dt < DT; ++dt)
+      o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][dt], pf, o[qb][dt], 0, 0, 0);
   };
-  // Softmax of one half of query block qb: mask (if needed), lazy max, P as bf16 in
-  // P.V key order.  Masked halves are scaled before the mask is applied (cs = 1
-  // afterwards) so that a zero softmax_scale cannot turn -inf into NaN; unmasked halves
-  // fold the scale into the exponent's FMA.
-  auto softmax = [&](f32x16_t& s, int k0h, int qb, bf16x8_t (&pf)[2]) {
+  // Softmax and P.V of one half of query block qb, in two 16-key steps (kk).  Masked
+  // halves are scaled before the mask is applied (cs = 1 afterwards) so that a zero
+  // softmax_scale cannot turn -inf into NaN; unmasked halves fold the scale into the
+  // exponent's FMA.  The running max m is raised lazily and without a max pass in the
+  // common case: a step's weights are taken against the current m, and only when some
+  // lane's sum of its 8 rounded weights exceeds kLazyBound (or is not finite: m = -inf
+  // before the first half) does the wave raise m to the max of the step's scores,
+  // rescale O and l, and take the weights again (key 0, visible to every query, lies in
+  // step 0 of the first half, so m is finite from then on).  Every weight is at most that sum, so no weight kept
+  // exceeds kLazyBound, the same headroom as testing the max itself.  A rescale in step
+  // 1 also scales step 0's P.V, which is already in O: that is the online softmax's own
+  // update.  Step 1's weights are computed while step 0's MFMAs run.
+  auto weights = [&](const f32x16_t& s, int kk, float cs, float mq, bf16x8_t& pf) {
+    float hs = 0.f;
+    u32x4_t w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = fast_exp2(fmaf(s[8 * kk + 2 * i], cs, -mq));
+      const float p1 = fast_exp2(fmaf(s[8 * kk + 2 * i + 1], cs, -mq));
+      w[i] = pack_bf16x2(p0, p1);
+      hs = dot2_bf16(w[i], ones, hs);
+    }
+    pf = __builtin_bit_cast(bf16x8_t, w);
+    return hs;
+  };
+  auto softmax_pv = [&](f32x16_t& s, int k0h, int qb, const bf16x8_t (&vf)[2][DT]) {
     const int qlo = wq0 + qb * 32;
     const bool masked = (k0h + 31 > diag + qlo) || (k0h + 32 > lk);
     const float cs = masked ? 1.0f : scale_log2e;
@@ -303,35 +327,30 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
         s[r] = (key < lk && key <= diag + qi) ? s[r] * scale_log2e : -INFINITY;
       }
     }
-    float x = s[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) x = fmaxf(x, s[r]);
-    const float mx = xor32_max(x) * cs;
-    if (__any(mx > m[qb] + kLazy)) {
-      const float mn = fmaxf(m[qb], mx);
-      const float alpha = fast_exp2(m[qb] - mn);
-      lsum[qb] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha;
-      m[qb] = mn;
-    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      u32x4_t w;
+      bf16x8_t pf;
+      float hs = weights(s, kk, cs, m[qb], pf);
+      if (__any(!(hs <= kLazyBound))) {
+        float x = s[8 * kk];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = fast_exp2(fmaf(s[8 * kk + 2 * i], cs, -m[qb]));
-        const float p1 = fast_exp2(fmaf(s[8 * kk + 2 * i + 1], cs, -m[qb]));
-        w[i] = pack_bf16x2(p0, p1);
-        lsum[qb] = dot2_bf16(w[i], ones, lsum[qb]);
+        for (int r = 1; r < 8; ++r) x = fmaxf(x, s[8 * kk + r]);
+        const float mn = fmaxf(m[qb], xor32_max(x) * cs);
+        const float alpha = fast_exp2(m[qb] - mn);
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha;
+        m[qb] = mn;
+        hs = weights(s, kk, cs, mn, pf);
       }
-      pf[kk] = __builtin_bit_cast(bf16x8_t, w);
+      lsum[qb] += hs;
+      pv(vf, qb, kk, pf);
     }
   };
   // One 32-key half for every query block: QK of all blocks first, then per block
   // softmax and P.V, so that each block's softmax runs beside MFMAs of another block.
   auto half = [&](const uint8_t* st, int kb, int k0h) {
-    bf16x8_t kf[KS], vf[2][DT], pf[2];
+    bf16x8_t kf[KS], vf[2][DT];
     f32x16_t s[QB];
     read_k(st, kb, kf);
     // all K fragment reads go out before the first MFMA, which then waits only for its
@@ -344,10 +363,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-      if (k0h < diag + min(wq0 + qb * 32 + 32, lq)) {   // this block sees some key of the half
-        softmax(s[qb], k0h, qb, pf);
-        pv(vf, qb, pf);
-      }
+      if (k0h < diag + min(wq0 + qb * 32 + 32, lq))   // this block sees some key of the half
+        softmax_pv(s[qb], k0h, qb, vf);
   };
 
   // ---- prologue: ids of tiles 0..2, tile 0 into stage 0 ----
@@ -471,11 +488,14 @@ prefill_f32_kernel(const float* __restrict__ q, int64_t q_row,
 
 template <int D, int G>
 static hipError_t launch_bf16(const PrefillArgs& a, hipStream_t st) {
-  constexpr int QB = 8 / NKV_PREFILL_QB >= G ? NKV_PREFILL_QB : 1;   // G must divide the waves
-  using Geo = PfGeom<D, G, QB>;
+  // G must divide the waves: the eight-wave kernel serves groups wider than the default
+  constexpr int NW0 = NKV_PREFILL_NW > G ? NKV_PREFILL_NW : G;
+  constexpr int QB = NW0 / NKV_PREFILL_QB >= G ? NKV_PREFILL_QB : 1;
+  constexpr int NW = NW0 / QB;
+  using Geo = PfGeom<D, G, QB, NW>;
   const PagedArgs& p = a.p;
   const int qtiles = (a.max_seqlen_q + Geo::BQ - 1) / Geo::BQ;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, QB>), dim3(p.num_seqs * p.num_kv_heads, qtiles),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, QB, NW>), dim3(p.num_seqs * p.num_kv_heads, qtiles),
                      dim3(Geo::NT), 0, st, static_cast<const uint16_t*>(a.q), a.q_row_elems,
                      static_cast<const uint16_t*>(p.k_cache), static_cast<const uint16_t*>(p.v_cache),
                      a.k_row_elems, a.v_row_elems, a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,

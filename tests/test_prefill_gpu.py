@@ -162,3 +162,22 @@ def test_prefill_deterministic_and_block_permutation_invariant():
                            case.cu_seqlens_q, case.cu_seqlens_k)
     out3 = gpu_prefill(case2)
     assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
+
+
+@pytest.mark.parametrize("direction", [1.0, -1.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_logits_ramp_forces_rescales(direction, dtype):
+    """Logits that rise (or fall) steadily along each sequence: the running max of the
+    online softmax moves many times per query (rising), or the later weights underflow
+    to zero (falling).  q = 3|N(0,1)| and k = 0.5 N(0,1) + direction * 2 * position / Lk
+    on every dim, so a query's scaled log2-logits span about 0..+-100 over its keys."""
+    dev = require_gpu()
+    shape = wl.Shape(32, 8, 128, 16 if dtype == "f32" else 256, dtype)
+    seqs = [(300, 300), (130, 130), (64, 400), (1, 257)]
+    case = random_prefill_case(800 + int(direction > 0), seqs, shape)
+    tdt = case.q.dtype
+    pos = np.concatenate([np.arange(lk - lq, lk) / lk for lq, lk in seqs]).astype(np.float32)
+    ramp = torch.as_tensor(pos, device=dev)[:, None, None] * (2.0 * direction)
+    case.q = (3.0 * case.q.float().abs()).to(tdt)
+    case.k = (0.5 * case.k.float() + ramp).to(tdt)
+    check(case, f"logit ramp {direction:+.0f} {dtype}")
