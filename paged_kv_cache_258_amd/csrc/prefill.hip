@@ -181,15 +181,18 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     const int phys = __builtin_amdgcn_readfirstlane(s_ids[t % 3][0]);
     return base + ((int64_t(phys) << log2_bs) + ((t * kBK) & bs_mask)) * stride;
   };
+  auto issue_k_at = [&](int t, const uint16_t* tb) {   // tile t inside one block at tb
+    uint8_t* sk = smem + (t % kStages) * Geo::STAGE;
+    const int rmax = lk - 1 - t * kBK;               // rows past the keys repeat the last
+#pragma unroll
+    for (int j = 0; j < Geo::K_DMA; ++j)
+      load_lds16(tb + min(k_row[j], rmax) * k_stride + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
+  };
   auto issue_k = [&](int t) {
     uint8_t* sk = smem + (t % kStages) * Geo::STAGE;
     const int rmax = lk - 1 - t * kBK;               // rows past the keys repeat the last
     if (tile_in_block) {
-      const uint16_t* tb = tile_base(t, kbase, k_stride);
-#pragma unroll
-      for (int j = 0; j < Geo::K_DMA; ++j)
-        load_lds16(tb + min(k_row[j], rmax) * k_stride + k_elem[j],
-                   sk + (wave * Geo::K_DMA + j) * 1024);
+      issue_k_at(t, tile_base(t, kbase, k_stride));
     } else {
 #pragma unroll
       for (int j = 0; j < Geo::K_DMA; ++j) {
@@ -202,16 +205,19 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const bool v_item = tid < Geo::V_ITEMS;
   const int v_kg = tid % (kBK / KPI), v_c = tid / (kBK / KPI);   // key group, 16-byte chunk
   u32x4_t vreg[KPI];
+  auto load_v_at = [&](int t, const uint16_t* tb) {     // tile t inside one block at tb
+    tb += v_c * 8;
+#pragma unroll
+    for (int j = 0; j < KPI; ++j) {
+      const int r = KPI * v_kg + j;
+      vreg[j] = (v_item && t * kBK + r < lk)          // rows past the keys are zero, not NaN
+                    ? *reinterpret_cast<const u32x4_t*>(tb + r * v_stride)
+                    : u32x4_t{0, 0, 0, 0};
+    }
+  };
   auto load_v = [&](int t) {
     if (tile_in_block) {
-      const uint16_t* tb = tile_base(t, vbase, v_stride) + v_c * 8;
-#pragma unroll
-      for (int j = 0; j < KPI; ++j) {
-        const int r = KPI * v_kg + j;
-        vreg[j] = (v_item && t * kBK + r < lk)        // rows past the keys are zero, not NaN
-                      ? *reinterpret_cast<const u32x4_t*>(tb + r * v_stride)
-                      : u32x4_t{0, 0, 0, 0};
-      }
+      load_v_at(t, tile_base(t, vbase, v_stride));
     } else {
 #pragma unroll
       for (int j = 0; j < KPI; ++j) {
@@ -367,14 +373,30 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
         softmax_pv(s[qb], k0h, qb, vf);
   };
 
-  // ---- prologue: ids of tiles 0..2, tile 0 into stage 0 ----
-  issue_ids(0);
-  if (ntiles > 1) issue_ids(1);
-  wait_vmem_all();
-  __syncthreads();
-  issue_k(0);
-  load_v(0);
-  if (ntiles > 2) issue_ids(2);
+  // ---- prologue: tile 0 into stage 0, ids of tiles 1..2 ----
+  if (tile_in_block) {
+    // tile 0's block id comes straight from the table (one scalar load), so its copies
+    // go out beside the q loads instead of after a round trip through s_ids
+    const uint16_t* k0b = kbase + kv0 * k_stride;
+    const uint16_t* v0b = vbase + kv0 * v_stride;
+    if (paged) {
+      const int64_t phys0 = __builtin_amdgcn_readfirstlane(trow[0]);
+      k0b = kbase + (phys0 << log2_bs) * k_stride;
+      v0b = vbase + (phys0 << log2_bs) * v_stride;
+    }
+    issue_k_at(0, k0b);
+    load_v_at(0, v0b);
+    if (ntiles > 1) issue_ids(1);
+    if (ntiles > 2) issue_ids(2);
+  } else {
+    issue_ids(0);
+    if (ntiles > 1) issue_ids(1);
+    wait_vmem_all();
+    __syncthreads();
+    issue_k(0);
+    load_v(0);
+    if (ntiles > 2) issue_ids(2);
+  }
   wait_vmem_all();
   commit_v(0);
   __syncthreads();

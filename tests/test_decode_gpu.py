@@ -229,3 +229,30 @@ def test_decode_long_pair_merged_over_several_chunks():
     # runs over several chunks with the running-maximum rescale between them.
     case = random_case(700, [40960], wl.QWEN3_8B)
     check(case, "one 40960-token sequence")
+
+
+@pytest.mark.parametrize("direction", [1.0, -1.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_logits_ramp_forces_rescales(direction, dtype):
+    """Logits that rise (or fall) steadily along each context: the running max moves many
+    times inside a piece (rising), later weights underflow (falling), and the pieces of a
+    cut pair carry maxima tens of log2 units apart into the merge.  q = 3|N(0,1)| and every
+    cached or new key is 0.5 N(0,1) + direction * 2 * position / L on every dim."""
+    dev = require_gpu()
+    shape = wl.Shape(32, 8, 128, 16 if dtype == "f32" else 256, dtype)
+    lens = [5000, 4096, 3001, 1000, 300, 17, 2, 1]
+    case = random_case(900 + int(direction > 0), lens, shape)
+    bs = shape.block_size
+    tdt = case.q.dtype
+    rows = case.k_cache.view(-1, shape.num_kv_heads, shape.head_dim)
+    for b, l in enumerate(lens):
+        if l > 1:
+            slots = torch.as_tensor(wl.slots_for_positions(case.block_table[b], np.arange(l - 1), bs)
+                                    .astype(np.int64), device=dev)
+            ramp = torch.arange(l - 1, device=dev, dtype=torch.float32)[:, None, None] * (2.0 * direction / l)
+            rows[slots] = (0.5 * rows[slots].float() + ramp).to(tdt)
+    new_ramp = torch.as_tensor([(l - 1) / l for l in lens], device=dev,
+                               dtype=torch.float32)[:, None, None] * (2.0 * direction)
+    case.k = (0.5 * case.k.float() + new_ramp).to(tdt)
+    case.q = (3.0 * case.q.float().abs()).to(tdt)
+    check(case, f"decode logit ramp {direction:+.0f} {dtype}")
