@@ -69,6 +69,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_c3_c4_counters.md")
+PREFILL_SOURCES = ["prefill.hip", "common.hpp", "launch.hpp"]
+PREFILL_CALLS = 12              # prefill calls per leg in the prefill counter pass (2 warm-up)
 COPY_BYTES = 1 << 30            # calibration copy: 1 GiB read + 1 GiB written per launch
 DECODE_KERNELS = ("decode_streamk_kernel", "decode_fixup_kernel")
 DECODE_SOURCES = ["decode.hip", "common.hpp", "launch.hpp"]
@@ -219,10 +222,11 @@ def bench_decode(dev, steps, warmup, graph=True):
                 graph_ms_step=graph_ms_step)
 
 
-def bench_prefill(dev, which, steps, warmup, settle_s=1.5):
+def prefill_inputs(dev, which):
+    """C3 or C4 inputs on the device: the case, its pools (C4's shared prefix already
+    stored), the index arrays as int32 device tensors and the output buffer."""
     import torch
     import paged_kv_cache_258_amd as nkv
-    from paged_kv_cache_258_amd import accounting as acc
     from paged_kv_cache_258_amd import workloads as wl
 
     prefix = None
@@ -230,14 +234,22 @@ def bench_prefill(dev, which, steps, warmup, settle_s=1.5):
         case = wl.c3_prefill(dev)
     else:
         prefix, case = wl.c4_prefix_chunk(dev)
-    sh = case.shape
     kc, vc = case.k_cache, case.v_cache
     if prefix is not None:
         pk, pv, ps = prefix
         nkv.nkv_store_kvcache(pk, pv, kc, vc, i32(ps, dev))
     cu_q, cu_k = i32(case.cu_seqlens_q, dev), i32(case.cu_seqlens_k, dev)
     table, slots = i32(case.block_table, dev), i32(case.slot_mapping, dev)
-    out = torch.empty_like(case.q)
+    return case, kc, vc, cu_q, cu_k, table, slots, torch.empty_like(case.q)
+
+
+def bench_prefill(dev, which, steps, warmup, settle_s=1.5):
+    import torch
+    import paged_kv_cache_258_amd as nkv
+    from paged_kv_cache_258_amd import accounting as acc
+
+    case, kc, vc, cu_q, cu_k, table, slots, out = prefill_inputs(dev, which)
+    sh = case.shape
 
     def step(ev=None):
         if ev is not None:
@@ -672,6 +684,170 @@ def summarize_counters(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
+def prefill_counter_pass(dev):
+    """Workload of a rocprofv3 --pmc pass for the prefill legs: the copy of known size,
+    then for C3 and C4 the store of the new tokens and PREFILL_CALLS prefill calls."""
+    import torch
+    import paged_kv_cache_258_amd as nkv
+    from paged_kv_cache_258_amd import accounting as acc
+
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    legs = {}
+    for which in ("C3", "C4"):
+        case, kc, vc, cu_q, cu_k, table, slots, out = prefill_inputs(dev, which)
+        nkv.nkv_store_kvcache(case.k, case.v, kc, vc, slots)
+        for _ in range(PREFILL_CALLS):
+            nkv.nkv_paged_attn_prefill(case.q, kc, vc, cu_q, cu_k, table, case.max_seqlen_q,
+                                       case.max_seqlen_k, case.shape.scale, out=out)
+        torch.cuda.synchronize()
+        legs[which] = acc.prefill_flops(case.cu_seqlens_q, case.cu_seqlens_k,
+                                        case.shape.num_q_heads, case.shape.head_dim)
+        del case, kc, vc, out
+    print(json.dumps({"prefill_counter_pass": True, "calls_per_leg": PREFILL_CALLS,
+                      "flop": legs}), flush=True)
+
+
+# Prefill legs told apart by grid (threads): (sequence x KV head) x q-tiles x 512.
+PREFILL_GRIDS = {"C3": 64 * 32 * 512, "C4": 128 * 8 * 512}
+PREFILL_FLOP = {"C3": 275012124672, "C4": 171865800704}
+# bytes the leg must read at least once: q, the K/V rows its sequences span (C4: the
+# shared prefix once, every chunk), the tables
+PREFILL_UNIQUE_READ = {"C3": 16384 * 32 * 128 * 2 + 2 * 16384 * 8 * 128 * 2,
+                       "C4": 8192 * 32 * 128 * 2 + 2 * (1024 + 16 * 512) * 8 * 128 * 2}
+
+
+def summarize_prefill_counters(paths):
+    """Write profiles/prefill_c3_c4_counters.md from the CSVs of --prefill-counter-pass."""
+    import csv
+    import statistics as stx
+
+    per = {}        # (leg, counter) -> per-dispatch values
+    dur = {}        # leg -> durations (us)
+    copy = {}       # counter -> per-launch values of the calibration copy
+    simds, xcc = None, 1
+    for path in paths:
+        seen = {}
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                key = (int(r["Dispatch_Id"]), r["Counter_Name"])
+                e = seen.setdefault(key, [r["Kernel_Name"], int(r["Grid_Size"]), 0.0,
+                                          int(r["End_Timestamp"]) - int(r["Start_Timestamp"])])
+                e[2] += float(r["Counter_Value"])
+        agent = os.path.join(os.path.dirname(path), os.path.basename(path).replace(
+            "counter_collection", "agent_info"))
+        if simds is None and os.path.exists(agent):
+            with open(agent, newline="") as f:
+                for r in csv.DictReader(f):
+                    if int(r.get("Simd_Count") or 0) > 0:
+                        simds = int(r["Simd_Count"])
+                        xcc = int(r.get("Num_Xcc") or 1)
+        by_leg = {}
+        for (disp, counter), (name, grid, val, ns) in sorted(seen.items()):
+            if "neg_kernel" in name:
+                copy.setdefault(counter, []).append(val)
+            if "prefill_bf16_kernel" not in name:
+                continue
+            leg = next((k for k, g in PREFILL_GRIDS.items() if g == grid), None)
+            if leg is None:
+                continue
+            by_leg.setdefault((leg, counter), []).append(val)
+            dur.setdefault((leg, path), {})[disp] = ns / 1e3
+        for k, v in by_leg.items():
+            per[k] = v[2:] if len(v) > 4 else v            # skip the warm-up calls
+    durs = {}
+    for (leg, _), d in dur.items():
+        v = list(d.values())
+        durs.setdefault(leg, []).extend(v[2:] if len(v) > 4 else v)
+    simds = simds or 1024
+
+    def m(leg, c):
+        v = per.get((leg, c))
+        return stx.mean(v) if v else None
+
+    lines = ["# Prefill counters: C3 and C4 (`prefill_bf16_kernel`), MFMA utilisation, LDS, L2 and HBM",
+             "",
+             f"Prefill sources sha {kernel_source_sha(PREFILL_SOURCES)} (`prefill.hip`, `common.hpp`, "
+             "`launch.hpp`).  Qwen3-8B heads (32 Q / 8 KV, head_dim 128), block_size 256, bf16.",
+             "",
+             "Commands (repo root, MI355X, ROCm 7.2; one rocprofv3 pass per counter group):",
+             ""]
+    for i, grp in enumerate(PREFILL_COUNTER_GROUPS):
+        lines.append(f"    rocprofv3 --pmc {' '.join(grp)} -d DIR{i} -o pass --output-format csv -- "
+                     "python bench.py --prefill-counter-pass")
+    lines += ["    python bench.py --summarize-prefill-counters DIR0/pass_counter_collection.csv "
+              "DIR1/pass_counter_collection.csv DIR2/pass_counter_collection.csv", "",
+              f"Each pass runs {PREFILL_CALLS} calls per leg; the first 2 are dropped.  Values are per "
+              "dispatch, summed over the chip; SQ_* cycle counters count shader-clock cycles "
+              "(SQ_WAVE_CYCLES, SQ_ACTIVE_INST_*, SQ_WAIT_* in units of 4 cycles), "
+              f"GRBM_GUI_ACTIVE counts GPU-busy cycles summed over the {xcc} XCDs; the chip has "
+              f"{simds} SIMDs.  The dispatches run one at a time under the counters, so their "
+              "durations are longer than bench.py's steady-state calls.", "",
+              "| counter | C3 | C4 |", "|---|---|---|"]
+    counters = [c for grp in PREFILL_COUNTER_GROUPS for c in grp]
+    for c in counters + ["duration_us"]:
+        vals = []
+        for leg in ("C3", "C4"):
+            x = stx.mean(durs[leg]) if c == "duration_us" and durs.get(leg) else m(leg, c)
+            vals.append("—" if x is None else (f"{x:,.2f}" if c == "duration_us" else f"{x:,.0f}"))
+        lines.append(f"| {c} | {vals[0]} | {vals[1]} |")
+    fetch_copy = stx.mean(copy["FETCH_SIZE"]) if copy.get("FETCH_SIZE") else None
+    factor = COPY_BYTES / (fetch_copy * 1024.0) if fetch_copy else None
+    lines += ["", "Derived:", "", "| figure | C3 | C4 |", "|---|---|---|"]
+
+    def row(label, f):
+        out = []
+        for leg in ("C3", "C4"):
+            try:
+                x = f(leg)
+            except (TypeError, ZeroDivisionError, KeyError):
+                x = None
+            out.append("—" if x is None else x)
+        lines.append(f"| {label} | {out[0]} | {out[1]} |")
+
+    d = lambda leg: stx.mean(durs[leg])
+    gui = lambda leg: m(leg, "GRBM_GUI_ACTIVE") / xcc          # busy cycles of one XCD
+    row("shader clock, MHz (GRBM_GUI_ACTIVE per XCD / duration)", lambda leg: f"{gui(leg) / d(leg):,.0f}")
+    row("TFLOP/s in the counted dispatches (algorithmic flop / duration)",
+        lambda leg: f"{PREFILL_FLOP[leg] / d(leg) / 1e6:,.1f}")
+    row("of the 2.5 PFLOP/s dense bf16 peak", lambda leg: f"{PREFILL_FLOP[leg] / d(leg) / 1e6 / MFMA_BF16_PEAK_TFLOPS:.3f}")
+    row("MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE per XCD)",
+        lambda leg: f"{m(leg, 'SQ_VALU_MFMA_BUSY_CYCLES') / (simds * gui(leg)):.3f}")
+    row("MFMA busy cycles / the flop's cycles at 1024 flop per SIMD-cycle",
+        lambda leg: f"{m(leg, 'SQ_VALU_MFMA_BUSY_CYCLES') / (PREFILL_FLOP[leg] / 1024):.3f}")
+    row("VALU-MFMA co-execution / MFMA busy",
+        lambda leg: f"{m(leg, 'SQ_VALU_MFMA_COEXEC_CYCLES') / m(leg, 'SQ_VALU_MFMA_BUSY_CYCLES'):.3f}")
+    row("LDS bank conflicts / LDS active (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)",
+        lambda leg: f"{m(leg, 'SQ_LDS_BANK_CONFLICT') / m(leg, 'SQ_LDS_IDX_ACTIVE'):.3f}")
+    row("LDS waits / all instruction waits (SQ_WAIT_INST_LDS / SQ_WAIT_INST_ANY)",
+        lambda leg: f"{m(leg, 'SQ_WAIT_INST_LDS') / m(leg, 'SQ_WAIT_INST_ANY'):.3f}")
+    row("L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))",
+        lambda leg: f"{m(leg, 'TCC_HIT_sum') / (m(leg, 'TCC_HIT_sum') + m(leg, 'TCC_MISS_sum')):.3f}")
+    row(f"HBM-side read bytes (FETCH_SIZE x {factor:.3f})" if factor else "HBM-side read bytes",
+        lambda leg: f"{m(leg, 'FETCH_SIZE') * 1024 * factor / 1e6:,.1f} MB")
+    row("... / bytes the leg must read once (q, K/V, tables)",
+        lambda leg: f"{m(leg, 'FETCH_SIZE') * 1024 * factor / PREFILL_UNIQUE_READ[leg]:.2f}")
+    lines += ["", f"Calibration: a torch.neg over {COPY_BYTES >> 20} MiB of bf16 reads {COPY_BYTES >> 20} MiB; "
+              f"FETCH_SIZE reads it as {fetch_copy:,.0f} KiB per launch." if fetch_copy else ""]
+    text = "\n".join(lines) + "\n"
+    with open(PREFILL_COUNTERS, "w") as f:
+        f.write(text)
+    print(text)
+
+
+PREFILL_COUNTER_GROUPS = [
+    ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES",
+     "SQ_WAIT_INST_ANY", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+    ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS",
+     "TCC_HIT_sum", "TCC_MISS_sum"],
+    ["FETCH_SIZE"],
+]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -684,9 +860,16 @@ def main():
                     help="copy calibration + decode leg only (run under rocprofv3 --pmc)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/decode_c2_counters.json from two --pmc passes")
+    ap.add_argument("--prefill-counter-pass", action="store_true",
+                    help="copy calibration + C3 and C4 prefill calls only (run under rocprofv3 --pmc)")
+    ap.add_argument("--summarize-prefill-counters", nargs=3, metavar="CSV",
+                    help="write profiles/prefill_c3_c4_counters.md from the three --pmc passes")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_prefill_counters:
+        summarize_prefill_counters(args.summarize_prefill_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -705,6 +888,9 @@ def main():
     torch.cuda.synchronize()
     if args.counter_pass:
         counter_pass(dev, args.steps, args.warmup)
+        return
+    if args.prefill_counter_pass:
+        prefill_counter_pass(dev)
         return
     d = bench_decode(dev, args.steps, args.warmup)
     prefill = []
