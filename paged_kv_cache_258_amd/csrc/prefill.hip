@@ -7,27 +7,27 @@
 // block_table=...)).  Query i of a segment with Lq queries and Lk keys sits at position
 // Lk - Lq + i and sees keys j <= Lk - Lq + i.
 //
-// bf16 path (dense contraction -> MFMA, v_mfma_f32_32x32x16_bf16):
-//   grid (seq * kv_head, q-tile), q-tiles dispatched longest-first.  A workgroup holds
-//   the G query heads of one KV head; each wave owns 64 queries of one head (two
-//   32-query MFMA column blocks), so every K or V fragment read from LDS feeds two
-//   MFMAs.  K/V tiles of 64 keys are gathered through the block table into a double
-//   buffered LDS stage shared by all waves: K rows are copied HBM -> LDS directly
-//   (global_load_lds, chunk c of row t at c ^ t to spread banks); V is loaded to
-//   registers and written transposed (dims x keys, key order permuted to match the
-//   accumulator layout of S^T), so both MFMA operands are 16-byte LDS reads.  The next
-//   tile's copies are in flight while the current tile is computed.
-//   Scores are computed transposed, S^T = K Q^T, so each lane owns one query: its row
-//   max needs one exchange with the lane 32 away, its row sum stays in the lane.  P goes
-//   from the S^T accumulators straight into the B operand of O^T += V^T P^T.  A tile is
-//   processed as two 32-key halves, each QK -> softmax -> PV in turn: holding both halves'
-//   scores at once does not fit the register file next to the O^T accumulators (it spills
-//   and runs ~1.4x slower), and the four waves of a CU interleave one another's MFMA and
-//   softmax phases anyway.  The softmax uses one
-//   FMA + exp2 per score (scale folded in), the running max is raised lazily (rescale
-//   only past 2^8 headroom, detected from the weights' sum), and the row sum is a dot2 of the rounded bf16 weights.
-//   Only tiles that cross the causal diagonal or the end of the keys are masked.  The
-//   output goes through LDS so each row is written as one contiguous run.
+// bf16 path (dense contraction -> MFMA, v_mfma_f32_16x16x32_bf16):
+//   grid (seq * kv_head, q-tile), q-tiles dispatched longest-first.  A workgroup of 8
+//   waves (two per SIMD) holds the G query heads of one KV head; each wave owns 32
+//   queries of one head, two 16-query MFMA column blocks.  K/V tiles of 128 keys are
+//   gathered through the block table into a double-buffered LDS stage shared by all
+//   waves: K rows are copied HBM -> LDS directly (global_load_lds, chunk c of row t at
+//   c ^ t to spread banks); V is loaded to registers and written transposed (dims x
+//   keys, key order permuted to match the accumulator layout of S^T), so both MFMA
+//   operands are 16-byte LDS reads.  The next tile's copies are in flight while the
+//   current tile is computed.
+//   Scores are computed transposed, S^T = K Q^T, in 16x16 blocks: a lane holds 4 keys of
+//   one query per block, so the max of a query spans four lanes and its row sum stays in
+//   the lanes until the end.  P goes from the S^T accumulators straight into the B
+//   operand of O^T += V^T P^T.  A tile is processed as four 32-key halves, each QK ->
+//   softmax -> PV; the 16x16 blocks let the softmax of the half's first key block start
+//   after 4 of the QK MFMAs instead of all of them (a 32x32 block needs every k-step).
+//   The softmax uses one FMA + exp2 per score (scale folded in), the running max is
+//   raised lazily (rescale only past 2^8 headroom, detected from the weights' sum), and
+//   the row sum is a dot2 of the rounded bf16 weights.  Only halves that cross the
+//   causal diagonal or the end of the keys are masked.  The output goes through LDS so
+//   each row is written as one contiguous run.
 // fp32 path: a plain VALU kernel (one lane per query and head, online softmax), used
 //   for correctness-sized fp32 inputs.
 #include <math.h>
@@ -37,9 +37,6 @@
 
 namespace nkv {
 
-#ifndef NKV_PREFILL_QB
-#define NKV_PREFILL_QB 1
-#endif
 #ifndef NKV_PREFILL_BK
 #define NKV_PREFILL_BK 128
 #endif
@@ -55,20 +52,18 @@ constexpr int kMaxIds = kBK / 16;       // block ids per tile (block_size >= 16)
 constexpr int kLog2BK = kBK == 128 ? 7 : 6;
 static_assert(kBK == 64 || kBK == 128, "64- or 128-key tiles");
 
-// QB: 32-query blocks per wave.  QB = 1: NKV_PREFILL_NW waves of 32 queries; QB = 2:
-// half as many waves of 64 queries, each K/V fragment read from LDS feeding two MFMAs.
 // Eight waves of 32 queries run two per SIMD inside one workgroup; four waves with
 // 64-key tiles (68 KB of LDS) let two workgroups share a CU, whose barriers, prologues
 // and epilogues are then independent of each other.
-template <int D, int G, int QB, int NWAVES>
+template <int D, int G, int NWAVES>
 struct PfGeom {
   static constexpr int NW = NWAVES;             // waves per workgroup
   static constexpr int NT = NW * kWave;
-  static constexpr int WQ = 32 * QB;            // queries per wave
+  static constexpr int WQ = 32;                 // queries per wave: two 16-query MFMA blocks
   static constexpr int QSUB = NW / G;           // query sub-tiles per workgroup
   static constexpr int BQ = WQ * QSUB;          // queries per workgroup
-  static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
-  static constexpr int DT = D / 32;             // 32-dim tiles of O^T
+  static constexpr int KS = D / 32;             // k-steps of S^T = K Q^T (32 dims each)
+  static constexpr int DT = D / 16;             // 16-dim tiles of O^T
   static constexpr int CPR = D / 8;             // 16-byte chunks per K row
   static constexpr int K_BYTES = kBK * D * 2;   // one K tile
   static constexpr int VROW = kBK + kVPad;      // Vt row stride (elements)
@@ -85,15 +80,16 @@ struct PfGeom {
   static constexpr int SMEM = kStages * STAGE > NW * WQ * OROW ? kStages * STAGE : NW * WQ * OROW;
 };
 
-// Position of key quad kq (keys 4kq..4kq+3) of a tile inside the transposed V rows:
-// within every 16-key step, bits 2 and 3 of the key index are swapped, which is the
-// order in which a 32x32 MFMA accumulator of S^T hands its keys to the P.V step.
+// Position of key quad kq (keys 4kq..4kq+3) of a tile inside the transposed V rows.
+// Within each 32-key half, key 16i + 4g + r (i: 16-key block, g: lane quarter, r < 4)
+// sits at 8g + 4i + r: the order in which the 16x16 S^T accumulators of the half's two
+// key blocks hand a lane its eight weights as the B operand of P.V.
 __device__ __forceinline__ int vt_quad_pos(int kq) {
-  return (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
+  return (kq & ~7) | ((kq & 3) << 1) | ((kq >> 2) & 1);
 }
 
-template <int D, int G, int QB, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2 / QB)))
+template <int D, int G, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                     int64_t k_stride, int64_t v_stride,
@@ -101,7 +97,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     const int32_t* __restrict__ block_table, int32_t max_blocks,
                     int32_t num_kv_heads, int32_t log2_bs, float scale_log2e,
                     uint16_t* __restrict__ out) {
-  using Geo = PfGeom<D, G, QB, NW>;
+  using Geo = PfGeom<D, G, NW>;
   constexpr int KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, VROW = Geo::VROW, WQ = Geo::WQ;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Geo::SMEM];
   __shared__ int32_t s_ids[3][kMaxIds];               // block ids of tiles t, t+1, t+2
@@ -123,8 +119,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int h = g * G + wave % G;
   if (NW == 8 && wave < 4) __builtin_amdgcn_s_setprio(3);   // waves 0-3 lead their SIMD partners
   const int hq = G * num_kv_heads;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
+  const int col = lane & 15;                          // MFMA column: query of a 16-block
+  const int quad = lane >> 4;                         // MFMA lane quarter
   const int wq0 = q0 + (wave / G) * WQ;               // this wave's first query
   const int kend = diag + min(q0 + Geo::BQ, lq);      // keys the workgroup needs
   const int ntiles = (kend + kBK - 1) / kBK;
@@ -140,17 +136,17 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const uint16_t* kbase = k_cache + int64_t(g) * D;
   const uint16_t* vbase = v_cache + int64_t(g) * D;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): per 32-query block, 8 dims per lane ----
-  bf16x8_t qf[QB][KS];
+  // ---- Q fragments (B operand of S^T = K Q^T): per 16-query block, 8 dims per lane ----
+  bf16x8_t qf[2][KS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = wq0 + qb * 32 + l32;
+  for (int j = 0; j < 2; ++j) {
+    const int qi = wq0 + 16 * j + col;
     const bool ok = qi < lq;
-    const uint16_t* qp = q + int64_t(qstart + (ok ? qi : 0)) * q_row + int64_t(h) * D + 8 * hh;
+    const uint16_t* qp = q + int64_t(qstart + (ok ? qi : 0)) * q_row + int64_t(h) * D + 8 * quad;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
-      qf[qb][ks] = __builtin_bit_cast(bf16x8_t, v);
+      const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 32) : u32x4_t{0, 0, 0, 0};
+      qf[j][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
@@ -253,124 +249,119 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     }
   };
 
-  f32x16_t o[QB][DT];
+  f32x4_t o[2][DT];                                   // O^T per (query block, 16 dims)
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][dt][r] = 0.f;
-  float m[QB], lsum[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    lsum[qb] = 0.f;
-  }
+    for (int dt = 0; dt < DT; ++dt) o[j][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
   const uint32_t ones = 0x3f803f80u;   // bf16 pair (1, 1)
 
-  // Fragments of the 32-key half `kb` of the tile in stage `st`: K rows (A operand of
-  // S^T = K Q^T) and V^T rows (A operand of O^T += V^T P^T), read ahead of their MFMAs.
-  auto read_k = [&](const uint8_t* st, int kb, bf16x8_t (&kf)[KS]) {
-    const int t = kb * 32 + l32;
+  // Fragments of the 32-key half `kb` of the tile in stage `st`: K rows of its two
+  // 16-key blocks (A operand of S^T = K Q^T) and V^T rows of its 16-dim tiles (A operand
+  // of O^T += V^T P^T), read ahead of their MFMAs.
+  auto read_k = [&](const uint8_t* st, int kb, bf16x8_t (&kf)[2][KS]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = *reinterpret_cast<const bf16x8_t*>(st + (t * CPR + ((2 * ks + hh) ^ (t & (CPR - 1)))) * 16);
+    for (int i = 0; i < 2; ++i) {
+      const int t = kb * 32 + 16 * i + col;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[i][ks] = *reinterpret_cast<const bf16x8_t*>(st + (t * CPR + ((4 * ks + quad) ^ (t & (CPR - 1)))) * 16);
+    }
   };
-  auto read_v = [&](const uint8_t* st, int kb, bf16x8_t (&vf)[2][DT]) {
+  auto read_v = [&](const uint8_t* st, int kb, bf16x8_t (&vf)[DT]) {
     const uint8_t* sv = st + Geo::K_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        vf[kk][dt] = *reinterpret_cast<const bf16x8_t*>(
-            sv + ((dt * 32 + l32) * VROW + kb * 32 + kk * 16 + 8 * hh) * 2);
+    for (int dt = 0; dt < DT; ++dt)
+      vf[dt] = *reinterpret_cast<const bf16x8_t*>(sv + ((dt * 16 + col) * VROW + kb * 32 + 8 * quad) * 2);
   };
-  auto qk = [&](const bf16x8_t (&kf)[KS], int qb, f32x16_t& s) {
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[qb][0], f32x16_t{}, 0, 0, 0);
+  auto qk = [&](const bf16x8_t (&kf)[KS], int j, f32x4_t& s) {
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[j][0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qb][ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[j][ks], s, 0, 0, 0);
   };
-  auto pv = [&](const bf16x8_t (&vf)[2][DT], int qb, int kk, const bf16x8_t& pf) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      o[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk][dt], pf, o[qb][dt], 0, 0, 0);
+  // Weights of one 16x16 block of S^T against max mq, as two bf16 pairs, and their sum.
+  auto weights = [&](const f32x4_t& s, float cs, float mq, uint32_t& w0, uint32_t& w1) {
+    w0 = pack_bf16x2(fast_exp2(fmaf(s[0], cs, -mq)), fast_exp2(fmaf(s[1], cs, -mq)));
+    w1 = pack_bf16x2(fast_exp2(fmaf(s[2], cs, -mq)), fast_exp2(fmaf(s[3], cs, -mq)));
+    return dot2_bf16(w1, ones, dot2_bf16(w0, ones, 0.f));
   };
-  // Softmax and P.V of one half of query block qb, in two 16-key steps (kk).  Masked
-  // halves are scaled before the mask is applied (cs = 1 afterwards) so that a zero
-  // softmax_scale cannot turn -inf into NaN; unmasked halves fold the scale into the
-  // exponent's FMA.  The running max m is raised lazily and without a max pass in the
-  // common case: a step's weights are taken against the current m, and only when some
-  // lane's sum of its 8 rounded weights exceeds kLazyBound (or is not finite: m = -inf
-  // before the first half) does the wave raise m to the max of the step's scores,
-  // rescale O and l, and take the weights again (key 0, visible to every query, lies in
-  // step 0 of the first half, so m is finite from then on).  Every weight is at most that sum, so no weight kept
-  // exceeds kLazyBound, the same headroom as testing the max itself.  A rescale in step
-  // 1 also scales step 0's P.V, which is already in O: that is the online softmax's own
-  // update.  Step 1's weights are computed while step 0's MFMAs run.
-  auto weights = [&](const f32x16_t& s, int kk, float cs, float mq, bf16x8_t& pf) {
-    float hs = 0.f;
-    u32x4_t w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p0 = fast_exp2(fmaf(s[8 * kk + 2 * i], cs, -mq));
-      const float p1 = fast_exp2(fmaf(s[8 * kk + 2 * i + 1], cs, -mq));
-      w[i] = pack_bf16x2(p0, p1);
-      hs = dot2_bf16(w[i], ones, hs);
-    }
-    pf = __builtin_bit_cast(bf16x8_t, w);
-    return hs;
-  };
-  auto softmax_pv = [&](f32x16_t& s, int k0h, int qb, const bf16x8_t (&vf)[2][DT]) {
-    const int qlo = wq0 + qb * 32;
-    const bool masked = (k0h + 31 > diag + qlo) || (k0h + 32 > lk);
+  // Softmax and P.V of one half.  s[i][j] is S^T of key block i and query block j; a
+  // lane holds keys 16i + 4*quad + r of query 16j + col.  Masked halves are scaled
+  // before the mask is applied (cs = 1 afterwards) so that a zero softmax_scale cannot
+  // turn -inf into NaN; unmasked halves fold the scale into the exponent's FMA.  The
+  // running max m is raised lazily and without a max pass in the common case: the
+  // weights are taken against the current m, and only when some lane's sum of its 8
+  // rounded weights of a query block exceeds kLazyBound (or is not finite: m = -inf
+  // before the first half) does the wave raise m to the max of the half's scores of
+  // that block (over the four lanes of each query), rescale O and l, and take the
+  // weights again.  Every weight is at most that sum, so no weight kept exceeds
+  // kLazyBound, the same headroom as testing the max itself.  Key 0, visible to every
+  // query, lies in the first half, so m is finite from then on.  Block 0's weights are
+  // computed while block 1's QK MFMAs run.
+  auto softmax_pv = [&](f32x4_t (&s)[2][2], int k0h, const bf16x8_t (&vf)[DT]) {
+    const bool masked = (k0h + 31 > diag + wq0) || (k0h + 32 > lk);
     const float cs = masked ? 1.0f : scale_log2e;
     if (masked) {
-      const int qi = qlo + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0h + 8 * (r >> 2) + 4 * hh + (r & 3);
-        s[r] = (key < lk && key <= diag + qi) ? s[r] * scale_log2e : -INFINITY;
-      }
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int qi = wq0 + 16 * j + col;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0h + 16 * i + 4 * quad + r;
+            s[i][j][r] = (key < lk && key <= diag + qi) ? s[i][j][r] * scale_log2e : -INFINITY;
+          }
+        }
     }
+    uint32_t w[2][2][2];
+    float hs[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t pf;
-      float hs = weights(s, kk, cs, m[qb], pf);
-      if (__any(!(hs <= kLazyBound))) {
-        float x = s[8 * kk];
+    for (int j = 0; j < 2; ++j) hs[j] = weights(s[0][j], cs, m[j], w[0][j][0], w[0][j][1]);
 #pragma unroll
-        for (int r = 1; r < 8; ++r) x = fmaxf(x, s[8 * kk + r]);
-        const float mn = fmaxf(m[qb], xor32_max(x) * cs);
-        const float alpha = fast_exp2(m[qb] - mn);
-        lsum[qb] *= alpha;
+    for (int j = 0; j < 2; ++j) hs[j] += weights(s[1][j], cs, m[j], w[1][j][0], w[1][j][1]);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha;
-        m[qb] = mn;
-        hs = weights(s, kk, cs, mn, pf);
+    for (int j = 0; j < 2; ++j) {
+      if (__any(!(hs[j] <= kLazyBound))) {
+        float x = s[0][j][0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r) x = fmaxf(x, s[0][j][r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x = fmaxf(x, s[1][j][r]);
+        const float mn = fmaxf(m[j], xor32_max(xor16_max(x)) * cs);
+        const float alpha = fast_exp2(m[j] - mn);
+        lsum[j] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[j][dt] *= alpha;
+        m[j] = mn;
+        hs[j] = weights(s[0][j], cs, mn, w[0][j][0], w[0][j][1]) +
+                weights(s[1][j], cs, mn, w[1][j][0], w[1][j][1]);
       }
-      lsum[qb] += hs;
-      pv(vf, qb, kk, pf);
+      lsum[j] += hs[j];
+      const u32x4_t pw = {w[0][j][0], w[0][j][1], w[1][j][0], w[1][j][1]};
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[j][dt], 0, 0, 0);
     }
   };
-  // One 32-key half for every query block: QK of all blocks first, then per block
-  // softmax and P.V, so that each block's softmax runs beside MFMAs of another block.
+  // One 32-key half: QK of key block 0 for both query blocks, then of key block 1 (the
+  // softmax of block 0 can run beside those MFMAs), then softmax and P.V.
   auto half = [&](const uint8_t* st, int kb, int k0h) {
-    bf16x8_t kf[KS], vf[2][DT];
-    f32x16_t s[QB];
+    bf16x8_t kf[2][KS], vf[DT];
+    f32x4_t s[2][2];
     read_k(st, kb, kf);
     // all K fragment reads go out before the first MFMA, which then waits only for its
     // own (left to itself the compiler reads one fragment, waits, multiplies, and so on)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-      if (k0h < diag + min(wq0 + qb * 32 + 32, lq)) qk(kf, qb, s[qb]);
-    read_v(st, kb, vf);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-      if (k0h < diag + min(wq0 + qb * 32 + 32, lq))   // this block sees some key of the half
-        softmax_pv(s[qb], k0h, qb, vf);
+      for (int j = 0; j < 2; ++j) qk(kf[i], j, s[i][j]);
+    read_v(st, kb, vf);
+    softmax_pv(s, k0h, vf);
   };
 
   // ---- prologue: tile 0 into stage 0, ids of tiles 1..2 ----
@@ -421,18 +412,17 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // ---- epilogue: O^T / l -> bf16 rows staged in LDS, then contiguous row writes ----
   uint8_t* ost = smem + wave * WQ * Geo::OROW;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    if (wq0 + qb * 32 < lq) {
-      const float inv = 1.0f / xor32_sum(lsum[qb]);   // the two lane halves hold different keys
+  for (int j = 0; j < 2; ++j) {
+    // the four lanes of a query hold different keys
+    const float inv = 1.0f / xor32_sum(xor16_sum(lsum[j]));
+    if (wq0 + 16 * j < lq) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = dt * 32 + 8 * r4 + 4 * hh;
-          const u32x2_t w = {pack_bf16x2(o[qb][dt][4 * r4 + 0] * inv, o[qb][dt][4 * r4 + 1] * inv),
-                             pack_bf16x2(o[qb][dt][4 * r4 + 2] * inv, o[qb][dt][4 * r4 + 3] * inv)};
-          *reinterpret_cast<u32x2_t*>(ost + (qb * 32 + l32) * Geo::OROW + d0 * 2) = w;
-        }
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d0 = dt * 16 + 4 * quad;
+        const u32x2_t w = {pack_bf16x2(o[j][dt][0] * inv, o[j][dt][1] * inv),
+                           pack_bf16x2(o[j][dt][2] * inv, o[j][dt][3] * inv)};
+        *reinterpret_cast<u32x2_t*>(ost + (16 * j + col) * Geo::OROW + d0 * 2) = w;
+      }
     }
   }
   __syncthreads();
@@ -511,13 +501,11 @@ prefill_f32_kernel(const float* __restrict__ q, int64_t q_row,
 template <int D, int G>
 static hipError_t launch_bf16(const PrefillArgs& a, hipStream_t st) {
   // G must divide the waves: the eight-wave kernel serves groups wider than the default
-  constexpr int NW0 = NKV_PREFILL_NW > G ? NKV_PREFILL_NW : G;
-  constexpr int QB = NW0 / NKV_PREFILL_QB >= G ? NKV_PREFILL_QB : 1;
-  constexpr int NW = NW0 / QB;
-  using Geo = PfGeom<D, G, QB, NW>;
+  constexpr int NW = NKV_PREFILL_NW > G ? NKV_PREFILL_NW : G;
+  using Geo = PfGeom<D, G, NW>;
   const PagedArgs& p = a.p;
   const int qtiles = (a.max_seqlen_q + Geo::BQ - 1) / Geo::BQ;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, QB, NW>), dim3(p.num_seqs * p.num_kv_heads, qtiles),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW>), dim3(p.num_seqs * p.num_kv_heads, qtiles),
                      dim3(Geo::NT), 0, st, static_cast<const uint16_t*>(a.q), a.q_row_elems,
                      static_cast<const uint16_t*>(p.k_cache), static_cast<const uint16_t*>(p.v_cache),
                      a.k_row_elems, a.v_row_elems, a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,
