@@ -43,6 +43,9 @@ namespace nkv {
 #ifndef NKV_PREFILL_NW
 #define NKV_PREFILL_NW 8
 #endif
+#ifndef NKV_PREFILL_PRIO
+#define NKV_PREFILL_PRIO 0
+#endif
 
 constexpr int kBK = NKV_PREFILL_BK;     // keys per tile (a multiple of 32)
 constexpr int kStages = 2;              // K/V tiles in LDS (one computed, one landing)
@@ -117,7 +120,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = g * G + wave % G;
-  if (NW == 8 && wave < 4) __builtin_amdgcn_s_setprio(3);   // waves 0-3 lead their SIMD partners
+  if (NKV_PREFILL_PRIO && NW == 8 && wave < 4) __builtin_amdgcn_s_setprio(3);   // waves 0-3 lead their SIMD partners
   const int hq = G * num_kv_heads;
   const int col = lane & 15;                          // MFMA column: query of a 16-block
   const int quad = lane >> 4;                         // MFMA lane quarter
