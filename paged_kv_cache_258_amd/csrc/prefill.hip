@@ -14,8 +14,8 @@
 //   gathered through the block table into a double-buffered LDS stage shared by all
 //   waves: K rows are copied HBM -> LDS directly (global_load_lds, chunk c of row t at
 //   c ^ t to spread banks); V is loaded to registers and written transposed (dims x
-//   keys, key order permuted to match the accumulator layout of S^T), so both MFMA
-//   operands are 16-byte LDS reads.  The next tile's copies are in flight while the
+//   keys, key order permuted to match the accumulator layout of S^T, chunks swizzled
+//   like K's), so both MFMA operands are 16-byte LDS reads.  The next tile's copies are in flight while the
 //   current tile is computed.
 //   Scores are computed transposed, S^T = K Q^T, in 16x16 blocks: a lane holds 4 keys of
 //   one query per block, so the max of a query spans four lanes and its row sum stays in
@@ -50,7 +50,6 @@ namespace nkv {
 constexpr int kBK = NKV_PREFILL_BK;     // keys per tile (a multiple of 32)
 constexpr int kStages = 2;              // K/V tiles in LDS (one computed, one landing)
 constexpr float kLazyBound = 256.0f;    // largest weight kept before rescaling (2^8 headroom)
-constexpr int kVPad = 8;                // bf16 elements of padding per Vt row in LDS
 constexpr int kMaxIds = kBK / 16;       // block ids per tile (block_size >= 16)
 constexpr int kLog2BK = kBK == 128 ? 7 : 6;
 static_assert(kBK == 64 || kBK == 128, "64- or 128-key tiles");
@@ -69,7 +68,8 @@ struct PfGeom {
   static constexpr int DT = D / 16;             // 16-dim tiles of O^T
   static constexpr int CPR = D / 8;             // 16-byte chunks per K row
   static constexpr int K_BYTES = kBK * D * 2;   // one K tile
-  static constexpr int VROW = kBK + kVPad;      // Vt row stride (elements)
+  static constexpr int VROW = kBK;              // Vt row stride (elements)
+  static constexpr int VCH = kBK / 8;           // 16-byte chunks per Vt row
   static constexpr int VT_BYTES = D * VROW * 2;
   static constexpr int STAGE = K_BYTES + VT_BYTES;
   static constexpr int K_DMA = K_BYTES / 1024 / NW;   // K copy instructions per wave per tile
@@ -82,6 +82,15 @@ struct PfGeom {
   static_assert(V_ITEMS <= NT, "one V item per thread");
   static constexpr int SMEM = kStages * STAGE > NW * WQ * OROW ? kStages * STAGE : NW * WQ * OROW;
 };
+
+// Element offset of position pos of Vt row r: 16-byte chunk c of row r sits at
+// c ^ (r mod chunks), as for K, so that the fragment reads (16 rows x 4 chunks per
+// instruction) spread over the LDS banks.  (Rows padded by 16 bytes instead put the 16x16
+// fragment reads in 2-way bank conflicts: 31% of LDS cycles.)
+template <int VCH>
+__device__ __forceinline__ int vt_off(int r, int pos) {
+  return r * (VCH * 8) + ((((pos >> 3) ^ r) & (VCH - 1)) << 3) + (pos & 7);
+}
 
 // Position of key quad kq (keys 4kq..4kq+3) of a tile inside the transposed V rows.
 // Within each 32-key half, key 16i + 4g + r (i: 16-key block, g: lane quarter, r < 4)
@@ -101,7 +110,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     int32_t num_kv_heads, int32_t log2_bs, float scale_log2e,
                     uint16_t* __restrict__ out) {
   using Geo = PfGeom<D, G, NW>;
-  constexpr int KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, VROW = Geo::VROW, WQ = Geo::WQ;
+  constexpr int KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, WQ = Geo::WQ;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Geo::SMEM];
   __shared__ int32_t s_ids[3][kMaxIds];               // block ids of tiles t, t+1, t+2
 
@@ -236,8 +245,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       for (int w = 0; w < 4; ++w) {                   // dims 2w, 2w+1 of the chunk
         const uint32_t lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
         const uint32_t hi = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-        *reinterpret_cast<uint32_t*>(&vt[(v_c * 8 + 2 * w) * VROW + pos]) = lo;
-        *reinterpret_cast<uint32_t*>(&vt[(v_c * 8 + 2 * w + 1) * VROW + pos]) = hi;
+        *reinterpret_cast<uint32_t*>(&vt[vt_off<Geo::VCH>(v_c * 8 + 2 * w, pos)]) = lo;
+        *reinterpret_cast<uint32_t*>(&vt[vt_off<Geo::VCH>(v_c * 8 + 2 * w + 1, pos)]) = hi;
       }
     } else {
       const int pos = 4 * vt_quad_pos(v_kg);
@@ -246,8 +255,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
         const uint32_t a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
         const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
         const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-        *reinterpret_cast<u32x2_t*>(&vt[(v_c * 8 + 2 * w) * VROW + pos]) = lo;
-        *reinterpret_cast<u32x2_t*>(&vt[(v_c * 8 + 2 * w + 1) * VROW + pos]) = hi;
+        *reinterpret_cast<u32x2_t*>(&vt[vt_off<Geo::VCH>(v_c * 8 + 2 * w, pos)]) = lo;
+        *reinterpret_cast<u32x2_t*>(&vt[vt_off<Geo::VCH>(v_c * 8 + 2 * w + 1, pos)]) = hi;
       }
     }
   };
@@ -272,11 +281,16 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
         kf[i][ks] = *reinterpret_cast<const bf16x8_t*>(st + (t * CPR + ((4 * ks + quad) ^ (t & (CPR - 1)))) * 16);
     }
   };
+  // Vt rows dt * 16 + col share col's swizzle, so a half's reads are one per-lane offset
+  // (v_lane[kb]) plus a constant per 16-dim tile.
+  int v_lane[kBK / 32];
+#pragma unroll
+  for (int kb = 0; kb < kBK / 32; ++kb) v_lane[kb] = vt_off<Geo::VCH>(col, kb * 32 + 8 * quad) * 2;
   auto read_v = [&](const uint8_t* st, int kb, bf16x8_t (&vf)[DT]) {
-    const uint8_t* sv = st + Geo::K_BYTES;
+    const uint8_t* sv = st + Geo::K_BYTES + v_lane[kb];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      vf[dt] = *reinterpret_cast<const bf16x8_t*>(sv + ((dt * 16 + col) * VROW + kb * 32 + 8 * quad) * 2);
+      vf[dt] = *reinterpret_cast<const bf16x8_t*>(sv + dt * 16 * Geo::VROW * 2);
   };
   auto qk = [&](const bf16x8_t (&kf)[KS], int j, f32x4_t& s) {
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[j][0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
