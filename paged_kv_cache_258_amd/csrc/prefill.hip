@@ -12,11 +12,11 @@
 //   waves (two per SIMD) holds the G query heads of one KV head; each wave owns 32
 //   queries of one head, two 16-query MFMA column blocks.  K/V tiles of 128 keys are
 //   gathered through the block table into a double-buffered LDS stage shared by all
-//   waves: K rows are copied HBM -> LDS directly (global_load_lds, chunk c of row t at
-//   c ^ t to spread banks); V is loaded to registers and written transposed (dims x
-//   keys, key order permuted to match the accumulator layout of S^T, chunks swizzled
-//   like K's), so both MFMA operands are 16-byte LDS reads.  The next tile's copies are in flight while the
-//   current tile is computed.
+//   waves: K and V rows are copied HBM -> LDS directly (global_load_lds, chunk c of row
+//   t at c ^ t to spread banks).  K fragments are 16-byte LDS reads; V^T fragments come
+//   from the transposing LDS read (ds_read_b64_tr_b16), two per fragment, in the key
+//   order of the P^T operand.  The next tile's copies are in flight while the current
+//   tile is computed.
 //   Scores are computed transposed, S^T = K Q^T, in 16x16 blocks: a lane holds 4 keys of
 //   one query per block, so the max of a query spans four lanes and its row sum stays in
 //   the lanes until the end.  P goes from the S^T accumulators straight into the B
@@ -47,6 +47,8 @@ namespace nkv {
 #define NKV_PREFILL_PRIO 0
 #endif
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;   // one transposing LDS read
+
 constexpr int kBK = NKV_PREFILL_BK;     // keys per tile (a multiple of 32)
 constexpr int kStages = 2;              // K/V tiles in LDS (one computed, one landing)
 constexpr float kLazyBound = 256.0f;    // largest weight kept before rescaling (2^8 headroom)
@@ -68,38 +70,14 @@ struct PfGeom {
   static constexpr int KS = D / 32;             // k-steps of S^T = K Q^T (32 dims each)
   static constexpr int DT = D / 16;             // 16-dim tiles of O^T
   static constexpr int CPR = D / 8;             // 16-byte chunks per K row
-  static constexpr int K_BYTES = kBK * D * 2;   // one K tile
-  static constexpr int VROW = kBK;              // Vt row stride (elements)
-  static constexpr int VCH = kBK / 8;           // 16-byte chunks per Vt row
-  static constexpr int VT_BYTES = D * VROW * 2;
-  static constexpr int STAGE = K_BYTES + VT_BYTES;
-  static constexpr int K_DMA = K_BYTES / 1024 / NW;   // K copy instructions per wave per tile
-  static constexpr int KPI = kBK * CPR / NT > 2 ? kBK * CPR / NT : 2;   // keys per V item
-  static_assert(KPI == 2 || KPI == 4, "V items of 2 or 4 keys");
-  static constexpr int V_ITEMS = (kBK / KPI) * CPR;   // (key group, chunk) items per tile
+  static constexpr int K_BYTES = kBK * D * 2;   // one K (or V) tile
+  static constexpr int STAGE = 2 * K_BYTES;     // K rows, then V rows, same layout
+  static constexpr int K_DMA = K_BYTES / 1024 / NW;   // copy instructions per wave per tile (K or V)
   static constexpr int OROW = D * 2 + 16;             // output staging row stride (bytes)
   static_assert(G >= 1 && G <= NW && NW % G == 0, "GQA group must divide the waves");
   static_assert(K_DMA >= 1 && K_BYTES % (1024 * NW) == 0, "K tile must split over the waves");
-  static_assert(V_ITEMS <= NT, "one V item per thread");
   static constexpr int SMEM = kStages * STAGE > NW * WQ * OROW ? kStages * STAGE : NW * WQ * OROW;
 };
-
-// Element offset of position pos of Vt row r: 16-byte chunk c of row r sits at
-// c ^ (r mod chunks), as for K, so that the fragment reads (16 rows x 4 chunks per
-// instruction) spread over the LDS banks.  (Rows padded by 16 bytes instead put the 16x16
-// fragment reads in 2-way bank conflicts: 31% of LDS cycles.)
-template <int VCH>
-__device__ __forceinline__ int vt_off(int r, int pos) {
-  return r * (VCH * 8) + ((((pos >> 3) ^ r) & (VCH - 1)) << 3) + (pos & 7);
-}
-
-// Position of key quad kq (keys 4kq..4kq+3) of a tile inside the transposed V rows.
-// Within each 32-key half, key 16i + 4g + r (i: 16-key block, g: lane quarter, r < 4)
-// sits at 8g + 4i + r: the order in which the 16x16 S^T accumulators of the half's two
-// key blocks hand a lane its eight weights as the B operand of P.V.
-__device__ __forceinline__ int vt_quad_pos(int kq) {
-  return (kq & ~7) | ((kq & 3) << 1) | ((kq >> 2) & 1);
-}
 
 template <int D, int G, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -190,74 +168,25 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     const int phys = __builtin_amdgcn_readfirstlane(s_ids[t % 3][0]);
     return base + ((int64_t(phys) << log2_bs) + ((t * kBK) & bs_mask)) * stride;
   };
-  auto issue_k_at = [&](int t, const uint16_t* tb) {   // tile t inside one block at tb
-    uint8_t* sk = smem + (t % kStages) * Geo::STAGE;
+  // K and V rows of tile t go HBM -> LDS directly, each into its half of stage t % 2
+  // (region 0: K, K_BYTES: V) in the same swizzled row layout.
+  auto issue_rows_at = [&](int t, const uint16_t* tb, int64_t stride, int region) {   // tile inside one block
+    uint8_t* sk = smem + (t % kStages) * Geo::STAGE + region;
     const int rmax = lk - 1 - t * kBK;               // rows past the keys repeat the last
 #pragma unroll
     for (int j = 0; j < Geo::K_DMA; ++j)
-      load_lds16(tb + min(k_row[j], rmax) * k_stride + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
+      load_lds16(tb + min(k_row[j], rmax) * stride + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
   };
-  auto issue_k = [&](int t) {
-    uint8_t* sk = smem + (t % kStages) * Geo::STAGE;
-    const int rmax = lk - 1 - t * kBK;               // rows past the keys repeat the last
+  auto issue_rows = [&](int t, const uint16_t* base, int64_t stride, int region) {
     if (tile_in_block) {
-      issue_k_at(t, tile_base(t, kbase, k_stride));
+      issue_rows_at(t, tile_base(t, base, stride), stride, region);
     } else {
+      uint8_t* sk = smem + (t % kStages) * Geo::STAGE + region;
+      const int rmax = lk - 1 - t * kBK;
 #pragma unroll
       for (int j = 0; j < Geo::K_DMA; ++j) {
         const int key = t * kBK + min(k_row[j], rmax);
-        load_lds16(kbase + row_off(t, key) + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
-      }
-    }
-  };
-  constexpr int KPI = Geo::KPI;
-  const bool v_item = tid < Geo::V_ITEMS;
-  const int v_kg = tid % (kBK / KPI), v_c = tid / (kBK / KPI);   // key group, 16-byte chunk
-  u32x4_t vreg[KPI];
-  auto load_v_at = [&](int t, const uint16_t* tb) {     // tile t inside one block at tb
-    tb += v_c * 8;
-#pragma unroll
-    for (int j = 0; j < KPI; ++j) {
-      const int r = KPI * v_kg + j;
-      vreg[j] = (v_item && t * kBK + r < lk)          // rows past the keys are zero, not NaN
-                    ? *reinterpret_cast<const u32x4_t*>(tb + r * v_stride)
-                    : u32x4_t{0, 0, 0, 0};
-    }
-  };
-  auto load_v = [&](int t) {
-    if (tile_in_block) {
-      load_v_at(t, tile_base(t, vbase, v_stride));
-    } else {
-#pragma unroll
-      for (int j = 0; j < KPI; ++j) {
-        const int key = t * kBK + KPI * v_kg + j;
-        vreg[j] = (v_item && key < lk)
-                      ? *reinterpret_cast<const u32x4_t*>(vbase + row_off(t, key) + v_c * 8)
-                      : u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
-  auto commit_v = [&](int t) {                        // KPI keys x 8 dims -> Vt
-    if (!v_item) return;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(smem + (t % kStages) * Geo::STAGE + Geo::K_BYTES);
-    if constexpr (KPI == 2) {
-      const int pos = 4 * vt_quad_pos(v_kg >> 1) + 2 * (v_kg & 1);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {                   // dims 2w, 2w+1 of the chunk
-        const uint32_t lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-        *reinterpret_cast<uint32_t*>(&vt[vt_off<Geo::VCH>(v_c * 8 + 2 * w, pos)]) = lo;
-        *reinterpret_cast<uint32_t*>(&vt[vt_off<Geo::VCH>(v_c * 8 + 2 * w + 1, pos)]) = hi;
-      }
-    } else {
-      const int pos = 4 * vt_quad_pos(v_kg);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {                   // dims 2w, 2w+1 of 4 keys each
-        const uint32_t a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
-        const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-        const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-        *reinterpret_cast<u32x2_t*>(&vt[vt_off<Geo::VCH>(v_c * 8 + 2 * w, pos)]) = lo;
-        *reinterpret_cast<u32x2_t*>(&vt[vt_off<Geo::VCH>(v_c * 8 + 2 * w + 1, pos)]) = hi;
+        load_lds16(base + row_off(t, key) + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
       }
     }
   };
@@ -282,16 +211,24 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
         kf[i][ks] = *reinterpret_cast<const bf16x8_t*>(st + (t * CPR + ((4 * ks + quad) ^ (t & (CPR - 1)))) * 16);
     }
   };
-  // Vt rows dt * 16 + col share col's swizzle, so a half's reads are one per-lane offset
-  // (v_lane[kb]) plus a constant per 16-dim tile.
-  int v_lane[kBK / 32];
-#pragma unroll
-  for (int kb = 0; kb < kBK / 32; ++kb) v_lane[kb] = vt_off<Geo::VCH>(col, kb * 32 + 8 * quad) * 2;
+  // V^T fragments by the transposing LDS read: in each 16-lane quarter, lane col addresses
+  // 4 dims (8 bytes) of key row 4*quad + (col >> 2) of a 16-key block, and the read hands
+  // it dim col of the quarter's 4 rows.  Two reads (key blocks 0 and 1) make the 8 keys
+  // 4*quad + r and 16 + 4*quad + r that the lane's P^T operand holds, in that order.
+  const int v_row = 4 * quad + (col >> 2), v_dim = 4 * (col & 3);
   auto read_v = [&](const uint8_t* st, int kb, bf16x8_t (&vf)[DT]) {
-    const uint8_t* sv = st + Geo::K_BYTES + v_lane[kb];
+    const uint8_t* sv = st + Geo::K_BYTES;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      vf[dt] = *reinterpret_cast<const bf16x8_t*>(sv + dt * 16 * Geo::VROW * 2);
+    for (int dt = 0; dt < DT; ++dt) {
+      s16x4_t h[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = kb * 32 + 16 * i + v_row, d = dt * 16 + v_dim;
+        const uint8_t* a = sv + (t * CPR + ((d >> 3) ^ (t & (CPR - 1)))) * 16 + (d & 7) * 2;
+        h[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
+      }
+      vf[dt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   };
   auto qk = [&](const bf16x8_t (&kf)[KS], int j, f32x4_t& s) {
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[j][0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -393,8 +330,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       k0b = kbase + (phys0 << log2_bs) * k_stride;
       v0b = vbase + (phys0 << log2_bs) * v_stride;
     }
-    issue_k_at(0, k0b);
-    load_v_at(0, v0b);
+    issue_rows_at(0, k0b, k_stride, 0);
+    issue_rows_at(0, v0b, v_stride, Geo::K_BYTES);
     if (ntiles > 1) issue_ids(1);
     if (ntiles > 2) issue_ids(2);
   } else {
@@ -402,19 +339,18 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     if (ntiles > 1) issue_ids(1);
     wait_vmem_all();
     __syncthreads();
-    issue_k(0);
-    load_v(0);
+    issue_rows(0, kbase, k_stride, 0);
+    issue_rows(0, vbase, v_stride, Geo::K_BYTES);
     if (ntiles > 2) issue_ids(2);
   }
   wait_vmem_all();
-  commit_v(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
     if (more) {                                   // next tile's copies fly during this one
-      issue_k(t + 1);
-      load_v(t + 1);
+      issue_rows(t + 1, kbase, k_stride, 0);
+      issue_rows(t + 1, vbase, v_stride, Geo::K_BYTES);
       if (t + 3 < ntiles) issue_ids(t + 3);
     }
     const int k0 = t * kBK;
@@ -423,7 +359,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     for (int kb = 0; kb < kBK / 32; ++kb)
       if (k0 + 32 * kb < wkend) half(st, kb, k0 + 32 * kb);
     wait_vmem_all();
-    if (more) commit_v(t + 1);
     __syncthreads();
   }
 
