@@ -52,6 +52,13 @@ Counter collection (two rocprofv3 passes, then a summary written to profiles/):
                                        DIR_W/pass_counter_collection.csv
 --counter-pass runs a plain elementwise copy (torch.neg over COPY_BYTES of bf16: reads
 and writes COPY_BYTES) three times, then the decode leg only.
+
+Prefill counters (three rocprofv3 passes, groups in PREFILL_COUNTER_GROUPS, then a summary
+written to profiles/prefill_c3_c4_counters.md):
+  rocprofv3 --pmc <group i> -d DIR<i> -o pass --output-format csv -- python bench.py --prefill-counter-pass
+  python bench.py --summarize-prefill-counters DIR0/... DIR1/... DIR2/pass_counter_collection.csv
+--prefill-counter-pass runs the same calibration copy, then PREFILL_CALLS prefill calls of
+C3 and of C4 (after storing their tokens).
 """
 
 from __future__ import annotations
