@@ -53,6 +53,26 @@ def test_rms_norm_hand_worked_example():
     assert np.array_equal(out, np.array([[0.84765625, 2.265625]], np.float32))
 
 
+def test_rms_norm_two_casts_hand_worked():
+    # The RMSNorm of 「同一个 Qwen3，两种写法」 §3.6 (add_rms_forward) casts the normalised
+    # value to the input dtype and only then multiplies by the weight in that dtype: two
+    # roundings to bf16.  x = (3, 4), w = (1, 1.5), eps = 0: x * r = (0.848528, 1.131371)
+    # -> bf16 (0.84765625, 1.1328125); 1.1328125 * 1.5 = 1.69921875 lies half-way between
+    # the bf16 neighbours 1.6953125 and 1.703125 and rounds to the even one, 1.703125.  A
+    # single rounding of x * r * w = 1.697056 would give 1.6953125 instead.
+    want = np.array([[0.84765625, 1.703125]], np.float32)
+    out = rn.rms_norm_ref(np.array([[3.0, 4.0]], np.float32), np.array([1.0, 1.5], np.float32), 0.0)
+    assert np.array_equal(out, want)
+    # the same through the residual add: x = (1, 2), r = (2, 2) sum to (3, 4)
+    xb = rn.f32_to_bf16_bits(np.array([[1.0, 2.0]], np.float32))
+    rb = rn.f32_to_bf16_bits(np.array([[2.0, 2.0]], np.float32))
+    wb = rn.f32_to_bf16_bits(np.array([1.0, 1.5], np.float32))
+    out2, resid = rn.add_rms_norm_ref(xb, rb, wb, 0.0)
+    assert np.array_equal(rn.bf16_bits_to_f32(resid), np.array([[3.0, 4.0]], np.float32))
+    assert np.array_equal(out2, np.array([[0x3F59, 0x3FDA]], np.uint16))   # 0.84765625, 1.703125
+    assert np.array_equal(rn.bf16_bits_to_f32(out2), want)
+
+
 def test_rms_norm_scale_invariance_and_unit_rms():
     rng = np.random.default_rng(12)
     x = rn.bf16_round(rng.standard_normal((64, 128)).astype(np.float32))
