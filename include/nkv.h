@@ -33,8 +33,8 @@
  * Ownership and ordering:
  *   - the caller owns every buffer; the library allocates nothing and keeps no state
  *     between calls (it caches the device's compute-unit count per device);
- *   - every call is asynchronous and ordered on `stream` (a hipStream_t passed as
- *     void*, NULL = the legacy default stream); nothing is read back to the host;
+ *   - every call is asynchronous and ordered on `stream` (NULL = the legacy default
+ *     stream); nothing is read back to the host;
  *   - outside checking mode a call allocates nothing, issues no memset and never
  *     synchronises, so it can be captured into a HIP graph (stream capture) and
  *     replayed; the decode work split is derived on the device from context_lens, so
@@ -77,6 +77,10 @@ extern "C" {
 #endif
 
 #define NKV_ABI_VERSION 1
+
+/* HIP's stream handle, declared here as HIP's own runtime header declares it, so that
+ * this header needs no HIP include (a repeated identical typedef is valid C11 / C++). */
+typedef struct ihipStream_t* hipStream_t;
 
 typedef enum {
   NKV_OK = 0,
@@ -124,7 +128,7 @@ nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_stride,
                                const int32_t* slot_mapping, int32_t num_tokens,
                                int32_t num_kv_heads, int32_t head_dim,
                                int32_t num_blocks, int32_t block_size,
-                               nkv_dtype_t dtype, void* stream);
+                               nkv_dtype_t dtype, hipStream_t stream);
 
 /*
  * Per-head RMSNorm of q and k, rotary embedding by position, and the KV store, in one
@@ -167,7 +171,7 @@ nkv_status_t nkv_qk_norm_rope_store(const void* qkv, int64_t qkv_row_stride,
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     void* q_out, void* k_cache, void* v_cache,
                                     int32_t num_blocks, int32_t block_size, nkv_dtype_t dtype,
-                                    void* stream);
+                                    hipStream_t stream);
 
 /*
  * Residual add + RMSNorm over token rows (bf16 only), the norm in front of each decoder
@@ -192,7 +196,7 @@ nkv_status_t nkv_qk_norm_rope_store(const void* qkv, int64_t qkv_row_stride,
  */
 nkv_status_t nkv_add_rms_norm(const void* x, const void* residual, const void* weight, float eps,
                               int32_t num_tokens, int32_t hidden_size, void* out,
-                              void* residual_out, nkv_dtype_t dtype, void* stream);
+                              void* residual_out, nkv_dtype_t dtype, hipStream_t stream);
 
 /*
  * Causal varlen prefill attention over the paged pools.
@@ -226,7 +230,7 @@ nkv_status_t nkv_paged_attn_prefill(const void* q, int64_t q_row_stride,
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t num_blocks, int32_t block_size,
                                     float softmax_scale, nkv_dtype_t dtype,
-                                    void* out, void* stream);
+                                    void* out, hipStream_t stream);
 
 /*
  * Causal varlen prefill over contiguous K/V: the branch without a prefix cache, where
@@ -255,7 +259,7 @@ nkv_status_t nkv_attn_varlen_prefill(const void* q, int64_t q_row_stride, const 
                                      int32_t max_seqlen_q, int32_t max_seqlen_k,
                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                      float softmax_scale, nkv_dtype_t dtype, void* out,
-                                     void* stream);
+                                     hipStream_t stream);
 
 /*
  * Bytes of device workspace nkv_paged_attn_decode needs for these sizes (partial
@@ -297,7 +301,7 @@ nkv_status_t nkv_paged_attn_decode(const void* q,
                                    int32_t head_dim, int32_t num_blocks, int32_t block_size,
                                    float softmax_scale, nkv_dtype_t dtype,
                                    void* out, void* workspace, size_t workspace_bytes,
-                                   void* stream);
+                                   hipStream_t stream);
 
 /*
  * ---- The CPU block manager (host memory and host code only; no device calls) ----

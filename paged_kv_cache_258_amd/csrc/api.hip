@@ -179,7 +179,7 @@ NKV_EXPORT nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_strid
                                           const int32_t* slot_mapping, int32_t num_tokens,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t num_blocks, int32_t block_size,
-                                          nkv_dtype_t dtype, void* stream) {
+                                          nkv_dtype_t dtype, hipStream_t stream) {
   if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (num_tokens < 0) return fail(NKV_ERR_INVALID_ARG, "num_tokens < 0");
   if (num_kv_heads <= 0 || head_dim <= 0) return fail(NKV_ERR_INVALID_ARG, "num_kv_heads and head_dim must be positive");
@@ -204,11 +204,11 @@ NKV_EXPORT nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_strid
   if (validating()) {
     nkv::ValidateResult r{};
     const hipError_t e = nkv::validate_store(slot_mapping, num_tokens, int64_t(num_blocks) * block_size,
-                                             static_cast<hipStream_t>(stream), &r);
+                                             stream, &r);
     const nkv_status_t vs = checked(e, r, "nkv_store_kvcache");
     if (vs != NKV_OK) return vs;
   }
-  return hip_status(nkv::launch_store(a, static_cast<hipStream_t>(stream)), "store launch");
+  return hip_status(nkv::launch_store(a, stream), "store launch");
 }
 
 NKV_EXPORT nkv_status_t nkv_qk_norm_rope_store(
@@ -216,7 +216,7 @@ NKV_EXPORT nkv_status_t nkv_qk_norm_rope_store(
     const void* k_norm_weight, const float* cos_sin_cache, int32_t max_position, float eps,
     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, void* q_out, void* k_cache, void* v_cache, int32_t num_blocks,
-    int32_t block_size, nkv_dtype_t dtype, void* stream) {
+    int32_t block_size, nkv_dtype_t dtype, hipStream_t stream) {
   if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (dtype != NKV_BF16) return fail(NKV_ERR_UNSUPPORTED, "q/k norm + rotary is implemented for bf16 only");
   if (num_tokens < 0) return fail(NKV_ERR_INVALID_ARG, "num_tokens < 0");
@@ -245,18 +245,18 @@ NKV_EXPORT nkv_status_t nkv_qk_norm_rope_store(
     nkv::ValidateResult r{};
     const hipError_t e = nkv::validate_rope_store(positions, slot_mapping, num_tokens, max_position,
                                                   int64_t(num_blocks) * block_size,
-                                                  static_cast<hipStream_t>(stream), &r);
+                                                  stream, &r);
     const nkv_status_t vs = checked(e, r, "nkv_qk_norm_rope_store");
     if (vs != NKV_OK) return vs;
   }
-  return hip_status(nkv::launch_qk_norm_rope_store(a, static_cast<hipStream_t>(stream)),
+  return hip_status(nkv::launch_qk_norm_rope_store(a, stream),
                     "q/k norm + rotary + store launch");
 }
 
 NKV_EXPORT nkv_status_t nkv_add_rms_norm(const void* x, const void* residual, const void* weight,
                                          float eps, int32_t num_tokens, int32_t hidden_size,
                                          void* out, void* residual_out, nkv_dtype_t dtype,
-                                         void* stream) {
+                                         hipStream_t stream) {
   if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (dtype != NKV_BF16) return fail(NKV_ERR_UNSUPPORTED, "residual add + RMSNorm is implemented for bf16 only");
   if (num_tokens < 0) return fail(NKV_ERR_INVALID_ARG, "num_tokens < 0");
@@ -281,7 +281,7 @@ NKV_EXPORT nkv_status_t nkv_add_rms_norm(const void* x, const void* residual, co
       return fail(NKV_ERR_INVALID_ARG, "an output overlaps an input other than as the same rows");
   }
   nkv::AddRmsNormArgs a{x, residual, weight, eps, num_tokens, hidden_size, out, residual_out, num_cus()};
-  return hip_status(nkv::launch_add_rms_norm(a, static_cast<hipStream_t>(stream)),
+  return hip_status(nkv::launch_add_rms_norm(a, stream),
                     "residual add + RMSNorm launch");
 }
 
@@ -291,7 +291,7 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_prefill(
     int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
     int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t num_blocks, int32_t block_size, float softmax_scale, nkv_dtype_t dtype, void* out,
-    void* stream) {
+    hipStream_t stream) {
   nkv::PrefillArgs a{};
   nkv_status_t st = check_paged(k_cache, v_cache, block_table, max_blocks_per_seq, num_seqs,
                                 num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
@@ -320,11 +320,11 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_prefill(
   a.out = out;
   if (validating()) {
     nkv::ValidateResult r{};
-    const hipError_t e = nkv::validate_prefill(a, total_q, -1, num_blocks, static_cast<hipStream_t>(stream), &r);
+    const hipError_t e = nkv::validate_prefill(a, total_q, -1, num_blocks, stream, &r);
     const nkv_status_t vs = checked(e, r, "nkv_paged_attn_prefill");
     if (vs != NKV_OK) return vs;
   }
-  return hip_status(nkv::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+  return hip_status(nkv::launch_prefill(a, stream), "prefill launch");
 }
 
 NKV_EXPORT nkv_status_t nkv_attn_varlen_prefill(
@@ -332,7 +332,7 @@ NKV_EXPORT nkv_status_t nkv_attn_varlen_prefill(
     int64_t v_row_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
     int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t head_dim, float softmax_scale, nkv_dtype_t dtype, void* out,
-    void* stream) {
+    hipStream_t stream) {
   if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(NKV_ERR_INVALID_ARG, "negative size");
@@ -386,11 +386,11 @@ NKV_EXPORT nkv_status_t nkv_attn_varlen_prefill(
   a.out = out;
   if (validating()) {
     nkv::ValidateResult r{};
-    const hipError_t e = nkv::validate_prefill(a, total_q, total_k, 0, static_cast<hipStream_t>(stream), &r);
+    const hipError_t e = nkv::validate_prefill(a, total_q, total_k, 0, stream, &r);
     const nkv_status_t vs = checked(e, r, "nkv_attn_varlen_prefill");
     if (vs != NKV_OK) return vs;
   }
-  return hip_status(nkv::launch_prefill(a, static_cast<hipStream_t>(stream)), "varlen prefill launch");
+  return hip_status(nkv::launch_prefill(a, stream), "varlen prefill launch");
 }
 
 NKV_EXPORT size_t nkv_paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -410,7 +410,7 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_decode(
     const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
     float softmax_scale, nkv_dtype_t dtype, void* out, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    hipStream_t stream) {
   nkv::DecodeArgs a{};
   nkv_status_t st = check_paged(k_cache, v_cache, block_table, max_blocks_per_seq, num_seqs,
                                 num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
@@ -433,9 +433,9 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_decode(
   a.workspace = workspace;
   if (validating()) {
     nkv::ValidateResult r{};
-    const hipError_t e = nkv::validate_decode(a, num_blocks, static_cast<hipStream_t>(stream), &r);
+    const hipError_t e = nkv::validate_decode(a, num_blocks, stream, &r);
     const nkv_status_t vs = checked(e, r, "nkv_paged_attn_decode");
     if (vs != NKV_OK) return vs;
   }
-  return hip_status(nkv::launch_decode(a, plan, static_cast<hipStream_t>(stream)), "decode launch");
+  return hip_status(nkv::launch_decode(a, plan, stream), "decode launch");
 }

@@ -232,7 +232,8 @@ __device__ __forceinline__ SkSplit make_split(int64_t R, int W) {
 // Descriptor of round t (per lane of a window): which pair, where, how long.
 struct SkWin {
   int b;      // sequence
-  int gl;     // KV head | (round inside the pair << 8)
+  int g;      // KV head
+  int local;  // round inside the pair
   int nr;     // rounds of the pair
 };
 
@@ -311,7 +312,8 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const int g = r / nr;
     const int local = r - g * nr;
     wn.b = lo;
-    wn.gl = g | (local << 8);
+    wn.g = g;
+    wn.local = local;
     wn.nr = nr;
     load_lds4(block_table + int64_t(lo) * max_blocks + ((local * kRound) >> log2_bs), &s_phys[slot][0]);
     load_lds4(context_lens + lo, &s_len[slot][0]);
@@ -326,22 +328,21 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   auto desc = [&](int64_t t) -> Desc {
     const int idx = int(t - wbase);
     Desc d;
-    int gl;
     if (idx < kSkWindow) {
       d.b = __builtin_amdgcn_readlane(wa.b, idx);
-      gl = __builtin_amdgcn_readlane(wa.gl, idx);
+      d.g = __builtin_amdgcn_readlane(wa.g, idx);
+      d.local = __builtin_amdgcn_readlane(wa.local, idx);
       d.nr = __builtin_amdgcn_readlane(wa.nr, idx);
       d.len = __builtin_amdgcn_readfirstlane(s_len[wcur][idx]);
       d.phys = __builtin_amdgcn_readfirstlane(s_phys[wcur][idx]);
     } else {
       d.b = __builtin_amdgcn_readlane(wb.b, idx - kSkWindow);
-      gl = __builtin_amdgcn_readlane(wb.gl, idx - kSkWindow);
+      d.g = __builtin_amdgcn_readlane(wb.g, idx - kSkWindow);
+      d.local = __builtin_amdgcn_readlane(wb.local, idx - kSkWindow);
       d.nr = __builtin_amdgcn_readlane(wb.nr, idx - kSkWindow);
       d.len = __builtin_amdgcn_readfirstlane(s_len[wcur ^ 1][idx - kSkWindow]);
       d.phys = __builtin_amdgcn_readfirstlane(s_phys[wcur ^ 1][idx - kSkWindow]);
     }
-    d.g = gl & 0xff;
-    d.local = gl >> 8;
     return d;
   };
 
@@ -497,12 +498,12 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(sc[i] - m);
-      l_part += p[i];
-    }
-    const s16x4_t pb = __builtin_bit_cast(
-        s16x4_t, (u32x2_t){pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m);
+    // the row sum adds the bf16-rounded weights that P.V multiplies, so the
+    // normalisation matches the weights actually applied
+    const uint32_t p01 = pack_bf16x2(p[0], p[1]), p23 = pack_bf16x2(p[2], p[3]);
+    l_part = dot2_bf16(p23, 0x3f803f80u, dot2_bf16(p01, 0x3f803f80u, l_part));
+    const s16x4_t pb = __builtin_bit_cast(s16x4_t, (u32x2_t){p01, p23});
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

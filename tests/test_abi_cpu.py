@@ -265,3 +265,31 @@ def test_varlen_prefill_rejects(lib, kw, status):
 def test_varlen_prefill_empty_is_noop(lib):
     assert varlen(lib, b=0, q=None, k=None, v=None, out=None) == _lib.NKV_OK
     assert varlen(lib, tq=0, mq=0, q=None) == _lib.NKV_OK
+
+
+def header_prototypes():
+    """name -> list of parameter declarations, from include/nkv.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(nkv_[a-z0-9_]+)\s*\(([^()]*)\)\s*;", text):
+        out[m.group(1)] = [" ".join(p.split()) for p in m.group(2).split(",")]
+    return out
+
+
+def test_stream_arguments_are_hip_streams():
+    # every call that launches work takes the stream last, as a hipStream_t
+    protos = header_prototypes()
+    launching = [n for n, ps in protos.items() if any("stream" in p for p in ps)]
+    assert set(launching) >= {"nkv_store_kvcache", "nkv_paged_attn_prefill", "nkv_paged_attn_decode",
+                              "nkv_attn_varlen_prefill", "nkv_qk_norm_rope_store", "nkv_add_rms_norm"}
+    for n in launching:
+        assert protos[n][-1] == "hipStream_t stream", (n, protos[n][-1])
+    assert "typedef struct ihipStream_t* hipStream_t;" in open(HEADER).read()
+
+
+def test_decode_workspace_query_signature():
+    # the query takes num_kv_heads beside the five call sizes (the stream-K plan
+    # counts rounds per KV head and sizes partial slots per GQA group)
+    assert header_prototypes()["nkv_paged_attn_decode_workspace_size"] == [
+        "int32_t num_seqs", "int32_t num_q_heads", "int32_t num_kv_heads", "int32_t head_dim",
+        "int32_t max_blocks_per_seq", "int32_t block_size"]
