@@ -6,7 +6,8 @@ it must match bit for bit.  The normalised output takes the same rounding points
 sides (cast to bf16 after the normalisation and after the weight product, float32 in
 between); what can still differ is the summation order of the row's mean square and the
 last bit of the reciprocal root, which moves an element across a bf16 rounding boundary
-now and then.  The bar: at least 99.5% of output elements bit-identical, and every
+now and then.  The bar: at most one output element in a thousand
+(and never fewer than one) differing from the oracle's bits, and every
 difference within 2^-6 of the largest |output| of its row (two bf16 units at that scale).
 
 Inputs (paged_kv_cache_258_amd.workloads.norm_rows): block outputs N(0, 1) times a per-row
@@ -40,7 +41,9 @@ def check(got_out, got_res, x_bits, r_bits, w_bits, what, res_written=True):
     bound = (2.0 ** -6) * np.abs(w).max(axis=-1, keepdims=True)
     worst = float((err / np.maximum(bound, 1e-30)).max()) if err.size else 0.0
     log(f"  {what}: bit-identical {same:.5f}, worst error / bound {worst:.3f}")
-    assert same >= 0.995, f"{what}: only {same:.5f} of elements bit-identical"
+    flips = int(np.count_nonzero(got_out != want_out))
+    # at most one element in a thousand (and never fewer than one) may differ
+    assert flips <= max(1, got_out.size // 1000), f"{what}: {flips} of {got_out.size} elements differ"
     assert np.all(err <= bound), f"{what}: error beyond two bf16 units of the row scale"
 
 

@@ -6,11 +6,14 @@
 
 Each layer has its own pools, block tables and values.  Layers 0, 17 and 35 are
 materialised at their full size and decoded exactly as bench.py launches them (the
-whole batch, default plan).  The oracle checks every sequence of C5a and a seeded
-sample of C5b (the longest, the shortest and six drawn at random), reading a compact
-host copy of just the sampled sequences' blocks with the block table renumbered to
-match (a gather of whole blocks: no arithmetic).
+whole batch, default plan).  The oracle checks every sequence of C5a, every sequence
+of C5b's layer 0 and a seeded sample of 32 C5b sequences on layers 17 and 35 (the
+longest, the shortest and thirty drawn at random), reading a compact host copy of just
+the checked sequences' blocks with the block table renumbered to match (a gather of
+whole blocks: no arithmetic).  The oracle runs one slice of sequences per worker thread.
 """
+
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -44,33 +47,47 @@ def compact(kc, vc, table, lens, seqs, bs):
     return kh, vh, sub
 
 
-def sample_seqs(kind, lens):
-    if kind == "a":
+def sample_seqs(kind, lens, layer):
+    if kind == "a" or layer == 0:
         return list(range(len(lens)))
-    rng = np.random.default_rng(2580)
+    rng = np.random.default_rng(2580 + layer)
     pick = {int(np.argmax(lens)), int(np.argmin(lens))}
-    while len(pick) < 8:
+    while len(pick) < 32:
         pick.add(int(rng.integers(len(lens))))
     return sorted(pick)
 
 
+def oracle_decode_threaded(q_bits, kh, vh, lens, sub, scale, workers=8):
+    n = len(lens)
+    parts = [np.arange(i, n, workers) for i in range(workers) if i < n]
+    out = np.zeros((n,) + q_bits.shape[1:], dtype=np.float64)
+
+    def one(idx):
+        return idx, ref.decode_ref(q_bits, kh, vh, lens, sub, scale, elem="bf16", seqs=idx)[idx]
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for idx, o in ex.map(one, parts):
+            out[idx] = o
+    return out
+
+
 @pytest.mark.parametrize("kind", ["a", "b"])
-def test_decode_c5_full_size_sampled(kind):
+def test_decode_c5_full_size(kind):
     dev = require_gpu()
     mld = wl.c5_decode(kind, dev, layers=LAYERS)
     sh = mld.shape
     lens = mld.context_lens
-    seqs = sample_seqs(kind, lens)
-    log(f"[decode C5{kind}] B={len(lens)} sum_ctx={int(lens.sum())} layers={LAYERS} "
-        f"checked seqs={seqs} (lens {[int(lens[b]) for b in seqs]})")
+    log(f"[decode C5{kind}] B={len(lens)} sum_ctx={int(lens.sum())} layers={LAYERS}")
     lens_d = dev_i32(lens, dev)
     for layer, (q, kc, vc, table) in zip(LAYERS, mld.layers):
+        seqs = sample_seqs(kind, lens, layer)
+        log(f"  layer {layer}: checking {len(seqs)} sequences")
         out = nkv_paged_attn_decode(q, kc, vc, lens_d, dev_i32(table, dev), sh.scale)
         torch.cuda.synchronize()
         got = to_f64(out)[seqs]
         kh, vh, sub = compact(kc, vc, table, lens, seqs, sh.block_size)
-        want = ref.decode_ref(host_bits(q)[seqs], kh, vh, lens[seqs], sub, sh.scale, elem="bf16")
-        assert_close(got, want, f"C5{kind} layer {layer}")
+        want = oracle_decode_threaded(host_bits(q)[seqs], kh, vh, lens[seqs], sub, sh.scale)
+        assert_close(got, want, f"C5{kind} layer {layer} ({len(seqs)} sequences)")
         del out, kh, vh
     del mld
     torch.cuda.empty_cache()

@@ -21,15 +21,15 @@ from _gpu_helpers import assert_close, dev_i32, elem, host_bits, log, require_gp
 pytestmark = pytest.mark.gpu
 
 
-def oracle_decode(case, seqs=None):
+def oracle_decode(case, seqs=None, scale=None):
     kb, vb = host_bits(case.k_cache), host_bits(case.v_cache)
     if case.k is not None:
         kb, vb = ref.store_ref(host_bits(case.k), host_bits(case.v), kb, vb, case.slot_mapping)
     return ref.decode_ref(host_bits(case.q), kb, vb, case.context_lens, case.block_table,
-                          case.shape.scale, elem=elem(case.q), seqs=seqs)
+                          case.shape.scale if scale is None else scale, elem=elem(case.q), seqs=seqs)
 
 
-def gpu_decode(case, kc=None, vc=None, table=None):
+def gpu_decode(case, kc=None, vc=None, table=None, scale=None):
     dev = case.q.device
     kc = case.k_cache.clone() if kc is None else kc
     vc = case.v_cache.clone() if vc is None else vc
@@ -37,7 +37,7 @@ def gpu_decode(case, kc=None, vc=None, table=None):
         nkv_store_kvcache(case.k, case.v, kc, vc, dev_i32(case.slot_mapping, dev))
     out = nkv_paged_attn_decode(case.q, kc, vc, dev_i32(case.context_lens, dev),
                                 dev_i32(case.block_table if table is None else table, dev),
-                                case.shape.scale)
+                                case.shape.scale if scale is None else scale)
     torch.cuda.synchronize()
     return out
 
@@ -72,11 +72,11 @@ def random_case(seed, lens, shape, bs_pad_blocks=1, extra_nan_block=False):
     return wl.DecodeCase("random", shape, q, k, v, slots, kc, vc, table, lens)
 
 
-def check(case, tag, seqs=None):
+def check(case, tag, seqs=None, scale=None):
     log(f"[decode] {tag}: B={len(case.context_lens)} shape={case.shape} "
         f"lens[:8]={case.context_lens[:8].tolist()}")
-    got = to_f64(gpu_decode(case))
-    want = oracle_decode(case, seqs)
+    got = to_f64(gpu_decode(case, scale=scale))
+    want = oracle_decode(case, seqs, scale=scale)
     if seqs is not None:
         got, want = got[list(seqs)], want[list(seqs)]
     return assert_close(got, want, tag)
@@ -256,3 +256,35 @@ def test_decode_logits_ramp_forces_rescales(direction, dtype):
     case.k = (0.5 * case.k.float() + new_ramp).to(tdt)
     case.q = (3.0 * case.q.float().abs()).to(tdt)
     check(case, f"decode logit ramp {direction:+.0f} {dtype}")
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,dtype", [
+    (32, 8, 128, 256, "bf16"),
+    (16, 4, 64, 16, "bf16"),
+    (4, 1, 64, 16, "f32"),
+    (32, 8, 128, 256, "f32"),
+])
+def test_decode_zero_scale(hq, hkv, d, bs, dtype):
+    # softmax_scale = 0: every cached key weighs the same, so the output is the mean of
+    # the sequence's V rows, also across the pieces of a cut pair
+    shape = wl.Shape(hq, hkv, d, bs, dtype)
+    case = random_case(1000 + d + bs, [1, 17, 300, 1025, 4096, 9000], shape)
+    check(case, f"softmax_scale 0, {shape}", scale=0.0)
+
+
+def test_decode_more_sequences_than_one_launch():
+    # Above 512 sequences the batch is decoded in launches of 512 (the per-sequence
+    # prefix sums live in LDS); sequences on both sides of the cut are compared.
+    rng = np.random.default_rng(1100)
+    lens = rng.integers(1, 700, size=1100).astype(np.int32)
+    lens[[0, 511, 512, 1023, 1024, 1099]] = [1, 699, 256, 1, 600, 333]
+    case = random_case(1101, lens, wl.QWEN3_8B)
+    check(case, "1100 sequences (three launches)")
+
+
+def test_decode_more_than_256_kv_heads():
+    # 300 KV heads (GQA group 1): the stream-K round descriptors carry the head and the
+    # round index in separate registers, so neither can spill into the other
+    shape = wl.Shape(300, 300, 64, 16, "bf16")
+    case = random_case(1200, [1, 40, 333, 17], shape)
+    check(case, "300 KV heads")

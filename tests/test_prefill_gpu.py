@@ -4,6 +4,8 @@ The GPU stores the new tokens with its kernel and attends through the block tabl
 the oracle stores into its own copy of the pool (store_ref) and runs prefill_ref.
 """
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -17,7 +19,7 @@ from _gpu_helpers import assert_close, dev_i32, elem, host_bits, log, require_gp
 pytestmark = pytest.mark.gpu
 
 
-def gpu_prefill(case, prefix=None, q=None):
+def gpu_prefill(case, prefix=None, q=None, scale=None):
     dev = case.q.device
     kc, vc = case.k_cache.clone(), case.v_cache.clone()
     if prefix is not None:
@@ -27,12 +29,15 @@ def gpu_prefill(case, prefix=None, q=None):
     out = nkv_paged_attn_prefill(case.q if q is None else q, kc, vc,
                                  dev_i32(case.cu_seqlens_q, dev), dev_i32(case.cu_seqlens_k, dev),
                                  dev_i32(case.block_table, dev), case.max_seqlen_q,
-                                 case.max_seqlen_k, case.shape.scale)
+                                 case.max_seqlen_k, case.shape.scale if scale is None else scale)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_prefill(case, prefix=None, seqs=None):
+def oracle_prefill(case, prefix=None, seqs=None, scale=None):
+    """The oracle's prefill of the sequences `seqs` (all by default), one sequence per
+    worker thread (numpy releases the interpreter lock inside its array kernels).
+    Returns (out rows of those sequences, their row indices in the batch)."""
     kb, vb = host_bits(case.k_cache), host_bits(case.v_cache)
     if prefix is not None:
         pk, pv, pslots = prefix
@@ -40,25 +45,27 @@ def oracle_prefill(case, prefix=None, seqs=None):
     kb, vb = ref.store_ref(host_bits(case.k), host_bits(case.v), kb, vb, case.slot_mapping)
     cu_q, cu_k = case.cu_seqlens_q, case.cu_seqlens_k
     q = host_bits(case.q)
-    if seqs is None:
-        return ref.prefill_ref(q, kb, vb, cu_q, cu_k, case.block_table, case.shape.scale,
-                               elem=elem(case.q)), None
-    rows = np.concatenate([np.arange(cu_q[b], cu_q[b + 1]) for b in seqs])
-    sub_cu_q = np.concatenate([[0], np.cumsum([cu_q[b + 1] - cu_q[b] for b in seqs])])
-    sub_cu_k = np.concatenate([[0], np.cumsum([cu_k[b + 1] - cu_k[b] for b in seqs])])
-    out = ref.prefill_ref(q[rows], kb, vb, sub_cu_q, sub_cu_k, case.block_table[list(seqs)],
-                          case.shape.scale, elem=elem(case.q))
-    return out, rows
+    scale = case.shape.scale if scale is None else scale
+    seqs = list(range(len(cu_q) - 1)) if seqs is None else list(seqs)
+
+    def one(b):
+        lq, lk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
+        return ref.prefill_ref(q[cu_q[b]:cu_q[b + 1]], kb, vb, np.array([0, lq]), np.array([0, lk]),
+                               case.block_table[b:b + 1], scale, elem=elem(case.q))
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        parts = list(ex.map(one, seqs))
+    rows = np.concatenate([np.arange(cu_q[b], cu_q[b + 1]) for b in seqs] + [np.zeros(0, np.int64)])
+    hq, d = case.q.shape[1], case.q.shape[2]
+    return np.concatenate(parts + [np.zeros((0, hq, d))]), rows
 
 
-def check(case, tag, prefix=None, seqs=None):
+def check(case, tag, prefix=None, seqs=None, scale=None):
     log(f"[prefill] {tag}: B={len(case.cu_seqlens_q) - 1} Tq={case.q.shape[0]} "
         f"maxq={case.max_seqlen_q} maxk={case.max_seqlen_k} shape={case.shape}")
-    got = to_f64(gpu_prefill(case, prefix))
-    want, rows = oracle_prefill(case, prefix, seqs)
-    if rows is not None:
-        got = got[rows]
-    return assert_close(got, want, tag)
+    got = to_f64(gpu_prefill(case, prefix, scale=scale))
+    want, rows = oracle_prefill(case, prefix, seqs, scale=scale)
+    return assert_close(got[rows], want, tag)
 
 
 def test_prefill_c1_tiny_fp32():
@@ -69,16 +76,16 @@ def test_prefill_c1_tiny_fp32():
     assert mx < 1e-4
 
 
-def test_prefill_c3_full_sampled_sequences():
+def test_prefill_c3_all_sequences():
     dev = require_gpu()
     case = wl.c3_prefill(dev)
-    check(case, "C3 8 x 2048, sequences 0 and 7", seqs=[0, 7])
+    check(case, "C3 8 x 2048, every sequence")
 
 
-def test_prefill_c4_prefix_chunk_sampled_sequences():
+def test_prefill_c4_prefix_chunk_all_sequences():
     dev = require_gpu()
     prefix, case = wl.c4_prefix_chunk(dev)
-    check(case, "C4 prefix 1024 + chunk 512, sequences 0, 5, 15", prefix=prefix, seqs=[0, 5, 15])
+    check(case, "C4 prefix 1024 + chunk 512, every sequence", prefix=prefix)
 
 
 def random_prefill_case(seed, seqs, shape):
@@ -181,3 +188,25 @@ def test_prefill_logits_ramp_forces_rescales(direction, dtype):
     case.q = (3.0 * case.q.float().abs()).to(tdt)
     case.k = (0.5 * case.k.float() + ramp).to(tdt)
     check(case, f"logit ramp {direction:+.0f} {dtype}")
+
+
+@pytest.mark.parametrize("bs", [512, 1024])
+def test_prefill_large_blocks(bs):
+    # block_size above the 128-key tile: a tile lies inside one block and its base is one
+    # scalar read; the tail of the last block is NaN and never read
+    shape = wl.Shape(32, 8, 128, bs, "bf16")
+    case = random_prefill_case(900 + bs, [(1, 1), (129, 129), (300, 1500), (700, 700), (64, 2100)], shape)
+    check(case, f"block_size {bs}")
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,dtype", [
+    (32, 8, 128, 256, "bf16"),
+    (16, 4, 64, 16, "bf16"),
+    (4, 1, 64, 16, "f32"),
+])
+def test_prefill_zero_scale(hq, hkv, d, bs, dtype):
+    # softmax_scale = 0: every visible key weighs the same, so each query's output is the
+    # mean of its visible V rows (the masked halves must not turn 0 * -inf into NaN)
+    shape = wl.Shape(hq, hkv, d, bs, dtype)
+    case = random_prefill_case(950 + d + bs, [(1, 1), (40, 40), (33, 300), (130, 130)], shape)
+    check(case, f"softmax_scale 0, {shape}", scale=0.0)

@@ -5,7 +5,8 @@ Both sides take the same rounding points (the listings' casts back to bf16 after
 normalisation, after the weight product and after the rotation, float32 in between); what
 can still differ is the summation order of a head's mean square and the last bit of its
 reciprocal root, which moves a normalised element across a bf16 rounding boundary now and
-then.  The bar, per output element: at least 99.5% of q/k elements bit-identical, and every
+then.  The bar, per output element: at most one q/k element in a thousand (and
+never fewer than one) differing from the oracle's bits, and every
 difference within 2^-6 of the largest |normed * weight| value of its head (two bf16 units
 at that scale).  v rows must be stored bit-exactly; pool rows that no slot names must stay
 untouched (NaN).
@@ -107,7 +108,9 @@ def compare(got_bits, want_bits, scale, what):
     bound = (2.0 ** -6) * np.broadcast_to(scale, err.shape)
     worst = float((err / np.maximum(bound, 1e-30)).max())
     log(f"  {what}: bit-identical {same:.5f}, worst error / bound {worst:.3f}")
-    assert same >= 0.995, f"{what}: only {same:.5f} of elements bit-identical"
+    flips = int(np.count_nonzero(got_bits != want_bits))
+    # at most one element in a thousand (and never fewer than one) may differ
+    assert flips <= max(1, got_bits.size // 1000), f"{what}: {flips} of {got_bits.size} elements differ"
     assert np.all(err <= bound), f"{what}: error beyond two bf16 units of the head scale"
 
 
