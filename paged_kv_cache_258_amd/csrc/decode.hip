@@ -184,8 +184,12 @@ struct SkGeom {
 
 // How the R rounds of a launch are cut into pieces.  The first Rs rounds are split
 // evenly over We persistent workgroups (stream-K); when every workgroup has enough
-// rounds, the last ~15% are cut into U units of L rounds that workgroups claim from a
-// counter once their own range is done, so that faster CUs take more of the tail.
+// rounds and the batch has at least as many (sequence, KV head) pairs as workgroups,
+// the last ~15% are cut into U units of L rounds that workgroups claim from a counter
+// once their own range is done, so that faster CUs take more of the tail.  With fewer
+// pairs than workgroups every pair is already cut into several pieces, and units would
+// cut the last pairs into many more (a 40960-token pair into ~160), each a partial for
+// the merge.
 // Piece p: p < We is workgroup p's range, p >= We is unit p - We.  The cuts depend
 // only on R and the grid, never on timing, so the merge order of partials is fixed.
 #ifndef NKV_SK_DYN_NUM
@@ -217,11 +221,11 @@ struct SkSplit {
   }
 };
 
-__device__ __forceinline__ SkSplit make_split(int64_t R, int W) {
+__device__ __forceinline__ SkSplit make_split(int64_t R, int W, int64_t pairs) {
   SkSplit sp;
   sp.R = R;
   sp.We = R < W ? int(R) : W;               // every static range non-empty
-  const int64_t Rd = R >= int64_t(kSkDynMinPerWg) * sp.We ? R * kSkDynNum / kSkDynDen : 0;
+  const int64_t Rd = R >= int64_t(kSkDynMinPerWg) * sp.We && pairs >= sp.We ? R * kSkDynNum / kSkDynDen : 0;
   const int64_t L = Rd > 0 ? (Rd + kSkMaxUnits - 1) / kSkMaxUnits : kSkUnitMin;
   sp.L = int(L > kSkUnitMin ? L : kSkUnitMin);
   sp.U = int((Rd + sp.L - 1) / sp.L);
@@ -291,7 +295,7 @@ decode_streamk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // Workers actually used: never more than there are rounds, so that every range is
   // non-empty (the grid is sized from an upper bound on the lengths).
   const int64_t R = int64_t(hkv) * s_prefix[num_seqs];
-  const SkSplit sp = make_split(R, W);
+  const SkSplit sp = make_split(R, W, int64_t(hkv) * num_seqs);
   if (w >= sp.We) return;
   // The unit counter starts at zero: zeroed here, long before any workgroup finishes
   // its own range and claims, and again by the fixup kernel after every launch.
@@ -587,7 +591,7 @@ decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_
   const int64_t R = int64_t(num_kv_heads) * prefix[num_seqs];
   const int nr = prefix[b + 1] - prefix[b];
   if (nr == 0 || R == 0) return;
-  const SkSplit sp = make_split(R, W);           // the stream-K kernel's pieces
+  const SkSplit sp = make_split(R, W, int64_t(num_kv_heads) * num_seqs);   // the stream-K kernel's pieces
   const int64_t s = int64_t(num_kv_heads) * prefix[b] + int64_t(g) * nr;   // first round
   const int64_t e = s + nr;                                               // past the last
   const int w0 = sp.piece(s), w1 = sp.piece(e - 1);
@@ -943,8 +947,16 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   if (wgs < 1) wgs = 1;
   p.wgs = int32_t(wgs);
   // partial slots: one pair of slots per workgroup range, plus per tail unit when the
-  // rounds can reach kSkDynMinPerWg per workgroup (the kernel's own condition)
-  p.pieces = p.wgs + (max_rounds >= int64_t(kSkDynMinPerWg) * p.wgs ? kSkMaxUnits : 0);
+  // kernel's own condition can hold (rounds can reach kSkDynMinPerWg per workgroup and
+  // the chunk has at least as many pairs as workgroups); units have >= kSkUnitMin rounds
+  const int64_t max_pairs = int64_t(num_kv_heads) * p.seq_chunk;
+  int64_t units = 0;
+  if (max_rounds >= int64_t(kSkDynMinPerWg) * p.wgs && max_pairs >= p.wgs) {
+    const int64_t rd = max_rounds * kSkDynNum / kSkDynDen;
+    units = (rd + kSkUnitMin - 1) / kSkUnitMin;
+    if (units > kSkMaxUnits) units = kSkMaxUnits;
+  }
+  p.pieces = int32_t(p.wgs + units);
   const size_t ws_bf16 = num_seqs <= 0 ? 0
                                        : align16(size_t(p.pieces) * 2 * grp * head_dim * sizeof(float)) +
                                              align16(size_t(p.pieces) * 2 * grp * 2 * sizeof(float)) +
