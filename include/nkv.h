@@ -304,6 +304,37 @@ nkv_status_t nkv_paged_attn_decode(const void* q,
                                    hipStream_t stream);
 
 /*
+ * Size of the device scratch that nkv_paged_attn_decode_noalloc uses in place of a
+ * workspace (a static device array: each device the library runs on holds one until the
+ * process ends).
+ */
+#define NKV_DECODE_SCRATCH_BYTES (64u << 20)
+
+/*
+ * nkv_paged_attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same operation, arguments, kernels and results (bit for bit) as
+ * nkv_paged_attn_decode; the partial results of split sequences go to the library's
+ * static device scratch of NKV_DECODE_SCRATCH_BYTES bytes instead of a caller's buffer.
+ *   - allocates nothing (no hipMalloc / hipFree, no allocating library call); the first
+ *     call on a device looks up that device's scratch address once;
+ *   - sizes whose workspace (nkv_paged_attn_decode_workspace_size) exceeds
+ *     NKV_DECODE_SCRATCH_BYTES are rejected with NKV_ERR_WORKSPACE before anything is
+ *     launched;
+ *   - every call on one device shares that device's scratch, which keeps the last call's
+ *     contents (the kernels need nothing cleared); calls that overlap on one device (other
+ *     streams, other threads) race on it and must be ordered by the caller.
+ */
+nkv_status_t nkv_paged_attn_decode_noalloc(const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* context_lens,
+                                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                                           float softmax_scale, nkv_dtype_t dtype,
+                                           void* out, hipStream_t stream);
+
+/*
  * ---- The CPU block manager (host memory and host code only; no device calls) ----
  *
  * The control plane that feeds the calls above: it hands out the blocks of a pool of

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     nkv_add_rms_norm,
     nkv_attn_varlen_prefill,
     nkv_paged_attn_decode,
+    nkv_paged_attn_decode_noalloc,
     nkv_paged_attn_decode_workspace_size,
     nkv_paged_attn_prefill,
     nkv_qk_norm_rope_store,
@@ -35,5 +36,6 @@ __all__ = [
     "nkv_paged_attn_prefill",
     "nkv_attn_varlen_prefill",
     "nkv_paged_attn_decode",
+    "nkv_paged_attn_decode_noalloc",
     "nkv_paged_attn_decode_workspace_size",
 ]

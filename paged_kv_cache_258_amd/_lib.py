@@ -31,6 +31,7 @@ EXPORTS = (
     "nkv_attn_varlen_prefill",
     "nkv_paged_attn_decode_workspace_size",
     "nkv_paged_attn_decode",
+    "nkv_paged_attn_decode_noalloc",
     "nkv_bm_create",
     "nkv_bm_destroy",
     "nkv_bm_num_free_blocks",
@@ -95,6 +96,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nkv_paged_attn_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32,
                                           c_i32, c_i32, c_i32, c_f, ctypes.c_int, c_p, c_p,
                                           ctypes.c_size_t, c_p]
+    lib.nkv_paged_attn_decode_noalloc.restype = ctypes.c_int
+    lib.nkv_paged_attn_decode_noalloc.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32,
+                                                  c_i32, c_i32, c_i32, c_f, ctypes.c_int, c_p, c_p]
     p_i32, p_i64, p_u64 = (ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
                            ctypes.POINTER(ctypes.c_uint64))
     pp = ctypes.POINTER(c_p)
@@ -347,6 +351,32 @@ def nkv_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                                      float(softmax_scale), _dtype(q), _ptr(out), _ptr(workspace),
                                      ws_bytes, _stream(q)),
            "nkv_paged_attn_decode")
+    return out
+
+
+def nkv_paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  context_lens: torch.Tensor, block_table: torch.Tensor,
+                                  softmax_scale: float, out: torch.Tensor) -> torch.Tensor:
+    """nkv_paged_attn_decode on the library's static device scratch (no workspace, no
+    allocation); the caller passes `out` [B, Hq, D]."""
+    lib = load()
+    nseq, hq, d = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    nb, bs, hkv, pd = _pool_dims(k_cache, v_cache)
+    if pd != d:
+        raise ValueError("head_dim of q and pools differ")
+    _int32_dev(context_lens, "context_lens")
+    _int32_dev(block_table, "block_table")
+    if context_lens.numel() != nseq or block_table.dim() != 2 or block_table.shape[0] != nseq:
+        raise ValueError("context_lens must be [B] and block_table [B, max_blocks]")
+    if out.shape != q.shape or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    _check(lib.nkv_paged_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(context_lens),
+                                             _ptr(block_table), block_table.shape[1], nseq, hq, hkv, d,
+                                             nb, bs, float(softmax_scale), _dtype(q), _ptr(out),
+                                             _stream(q)),
+           "nkv_paged_attn_decode_noalloc")
     return out
 
 

@@ -405,12 +405,45 @@ NKV_EXPORT size_t nkv_paged_attn_decode_workspace_size(int32_t num_seqs, int32_t
       .workspace_bytes;
 }
 
-NKV_EXPORT nkv_status_t nkv_paged_attn_decode(
-    const void* q, const void* k_cache, const void* v_cache, const int32_t* context_lens,
-    const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
-    float softmax_scale, nkv_dtype_t dtype, void* out, void* workspace, size_t workspace_bytes,
-    hipStream_t stream) {
+// Scratch of the allocation-free decode: a file-scope device array, one copy per device,
+// held until the process ends.  Host code never names it directly (in host code the
+// symbol is a host-side stand-in, not a device address): its device address is looked up
+// once per device with that device current, and that pointer is what the kernels get.
+// Its contents on entry do not matter to the decode kernels (the tail-unit counter is
+// reset by the kernels themselves), so nothing is cleared between calls.
+static __device__ __align__(256) uint8_t scratch[NKV_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device.
+nkv_status_t scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {nullptr};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(NKV_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table covers", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(NKV_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return NKV_OK;
+}
+
+// Decode with the workspace given (the caller's buffer, or the library's static scratch).
+nkv_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* context_lens, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                         int32_t block_size, float softmax_scale, nkv_dtype_t dtype, void* out,
+                         void* workspace, size_t workspace_bytes, bool scratch, hipStream_t stream) {
   nkv::DecodeArgs a{};
   nkv_status_t st = check_paged(k_cache, v_cache, block_table, max_blocks_per_seq, num_seqs,
                                 num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
@@ -422,6 +455,16 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_decode(
   const nkv::DecodePlan plan = nkv::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                 max_blocks_per_seq, block_size, a.p.num_cus);
   if (plan.workspace_bytes > 0) {
+    if (scratch) {   // the library's static scratch stands in for the caller's workspace
+      if (plan.workspace_bytes > size_t(NKV_DECODE_SCRATCH_BYTES))
+        return fail(NKV_ERR_WORKSPACE,
+                    "decode of these sizes needs %zu bytes of scratch; the library's static scratch holds %zu "
+                    "(use nkv_paged_attn_decode with a workspace)",
+                    plan.workspace_bytes, size_t(NKV_DECODE_SCRATCH_BYTES));
+      const nkv_status_t ss = scratch_ptr(&workspace);
+      if (ss != NKV_OK) return ss;
+      workspace_bytes = size_t(NKV_DECODE_SCRATCH_BYTES);
+    }
     if (!workspace || workspace_bytes < plan.workspace_bytes)
       return fail(NKV_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.workspace_bytes,
                   workspace ? workspace_bytes : size_t(0));
@@ -438,4 +481,27 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_decode(
     if (vs != NKV_OK) return vs;
   }
   return hip_status(nkv::launch_decode(a, plan, stream), "decode launch");
+}
+
+}  // namespace
+
+NKV_EXPORT nkv_status_t nkv_paged_attn_decode(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* context_lens,
+    const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+    float softmax_scale, nkv_dtype_t dtype, void* out, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, context_lens, block_table, max_blocks_per_seq, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, softmax_scale, dtype,
+                     out, workspace, workspace_bytes, false, stream);
+}
+
+NKV_EXPORT nkv_status_t nkv_paged_attn_decode_noalloc(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* context_lens,
+    const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+    float softmax_scale, nkv_dtype_t dtype, void* out, hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, context_lens, block_table, max_blocks_per_seq, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, softmax_scale, dtype,
+                     out, nullptr, 0, true, stream);
 }

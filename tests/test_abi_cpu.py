@@ -122,6 +122,42 @@ def test_decode_workspace_size(lib):
     assert f(64, 32, 8, 128, 32, 256) >= big
 
 
+def decode_noalloc(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, table=FAKE, maxb=16, b=64, hq=32, hkv=8,
+             d=128, nb=600, bs=256, scale=0.088, dtype=1, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.nkv_paged_attn_decode_noalloc(a["q"], a["kc"], a["vc"], a["lens"], a["table"],
+                                             a["maxb"], a["b"], a["hq"], a["hkv"], a["d"], a["nb"],
+                                             a["bs"], a["scale"], a["dtype"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=30), _lib.NKV_ERR_INVALID_ARG),
+    (dict(q=None), _lib.NKV_ERR_INVALID_ARG),
+    (dict(out=MISALIGNED), _lib.NKV_ERR_INVALID_ARG),
+    (dict(d=96), _lib.NKV_ERR_UNSUPPORTED),
+    # beyond the static scratch: 4096 fp32 sequences of up to 65536 tokens need far more
+    # than NKV_DECODE_SCRATCH_BYTES of partials
+    (dict(b=4096, maxb=256, dtype=0), _lib.NKV_ERR_WORKSPACE),
+])
+def test_decode_noalloc_rejects_before_launch(lib, kw, status):
+    assert lib.nkv_paged_attn_decode_workspace_size(4096, 32, 8, 128, 256, 256) > 64 << 20
+    assert decode_noalloc(lib, **kw) == status
+    assert lib.nkv_last_error() != b""
+    if status == _lib.NKV_ERR_WORKSPACE:
+        assert b"scratch" in lib.nkv_last_error()
+
+
+def test_decode_noalloc_zero_sequences_is_noop(lib):
+    assert decode_noalloc(lib, b=0, q=None, lens=None, out=None) == _lib.NKV_OK
+
+
+def test_decode_scratch_size_in_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define NKV_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == 64 << 20
+
+
 def prefill(lib, **kw):
     a = dict(q=FAKE, qs=4096, kc=FAKE, vc=FAKE, cuq=FAKE, cuk=FAKE, table=FAKE, maxb=8, b=8,
              tq=16384, mq=2048, mk=2048, hq=32, hkv=8, d=128, nb=64, bs=256, scale=0.088,
