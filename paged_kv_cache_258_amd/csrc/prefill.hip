@@ -169,10 +169,33 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     return base + ((int64_t(phys) << log2_bs) + ((t * kBK) & bs_mask)) * stride;
   };
   // K and V rows of tile t go HBM -> LDS directly, each into its half of stage t % 2
-  // (region 0: K, K_BYTES: V) in the same swizzled row layout.
+  // (region 0: K, K_BYTES: V) in the same swizzled row layout.  Inside a tile the rows
+  // are at most kBK - 1 strides from its base; with strides below 2^23 elements the byte
+  // offsets fit 32 bits, so a copy is a wave-uniform base plus a per-lane offset fixed
+  // for the whole kernel (full tiles) instead of 64-bit lane arithmetic (C3 310 -> 304 us).
+  const bool off32 = k_stride < (int64_t(1) << 23) && v_stride < (int64_t(1) << 23);
+  uint32_t koff[Geo::K_DMA], voff[Geo::K_DMA];
+#pragma unroll
+  for (int j = 0; j < Geo::K_DMA; ++j) {
+    koff[j] = uint32_t((k_row[j] * k_stride + k_elem[j]) * 2);
+    voff[j] = uint32_t((k_row[j] * v_stride + k_elem[j]) * 2);
+  }
   auto issue_rows_at = [&](int t, const uint16_t* tb, int64_t stride, int region) {   // tile inside one block
     uint8_t* sk = smem + (t % kStages) * Geo::STAGE + region;
     const int rmax = lk - 1 - t * kBK;               // rows past the keys repeat the last
+    if (off32) {
+      if (rmax >= kBK - 1) {
+#pragma unroll
+        for (int j = 0; j < Geo::K_DMA; ++j)
+          load_lds16_s(tb, region == 0 ? koff[j] : voff[j], sk + (wave * Geo::K_DMA + j) * 1024);
+      } else {
+#pragma unroll
+        for (int j = 0; j < Geo::K_DMA; ++j)
+          load_lds16_s(tb, uint32_t((min(k_row[j], rmax) * stride + k_elem[j]) * 2),
+                       sk + (wave * Geo::K_DMA + j) * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < Geo::K_DMA; ++j)
       load_lds16(tb + min(k_row[j], rmax) * stride + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
