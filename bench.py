@@ -22,7 +22,14 @@ the stream it runs on: algorithmic decode bytes / average duration vs 8 TB/s.
 traffic = HBM bytes per decode call measured by rocprofv3 counters (FETCH_SIZE and
 WRITE_SIZE, calibrated on a plain copy of known size), read from
 profiles/decode_c2_counters.json when it was taken on the current decode sources.
-cpu_baseline = the float64 CPU oracle (store_ref + decode_ref) on the same C2 batch.
+cpu_baseline = the float64 CPU oracle (store_ref + decode_ref) on the same C2 batch, with the
+host's CPU model; each long-context leg carries its own cpu_baseline: decode_ref over the
+full layer 0 (C5a: 4 sequences, C5b: all 256), per layer and x36 "extrapolated".
+engine_clock = the GPU engine clock the driver reports (pp_dpm_sclk), sampled every 2 ms
+while the decode graph steps are timed and while each prefill leg settles and is timed.
+prefill[i].roofline = the leg's algorithmic TFLOP/s against the dense bf16 MFMA peak, with
+MFMA busy, VALU-MFMA co-execution and HBM traffic (FETCH_SIZE, calibrated) from
+profiles/prefill_c3_c4_counters.json when it was taken on the current prefill sources.
 decode_call / prefill_call / store_call = mean, median and minimum of the per-call event times; the
 prefill legs' headline times (the prefill and the store before it) are the median calls.
 Prefill legs are timed in steady state: after the warm-up calls, 10 calls are timed at once
@@ -77,6 +84,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
 PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_c3_c4_counters.md")
+PREFILL_COUNTERS_JSON = os.path.join(ROOT, "profiles", "prefill_c3_c4_counters.json")
+SCLK_FILES = ("/sys/class/drm/card0/device/pp_dpm_sclk", "/sys/class/drm/card1/device/pp_dpm_sclk")
 PREFILL_SOURCES = ["prefill.hip", "common.hpp", "launch.hpp"]
 PREFILL_CALLS = 12              # prefill calls per leg in the prefill counter pass (2 warm-up)
 COPY_BYTES = 1 << 30            # calibration copy: 1 GiB read + 1 GiB written per launch
@@ -128,6 +137,95 @@ def kernel_source_sha(files) -> str:
         with open(os.path.join(ROOT, "paged_kv_cache_258_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Samples the GPU engine clock the driver reports (the current level of
+    pp_dpm_sclk, marked '*') every few milliseconds in a background thread, while the
+    timed calls run.  Gives the median / min / max MHz of the samples, or None where the
+    file is not readable."""
+
+    def __init__(self, period_s=0.002):
+        import threading
+        self.path = next((f for f in SCLK_FILES if os.access(f, os.R_OK)), None)
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def parse(text):
+        for line in text.splitlines():
+            if line.rstrip().endswith("*"):
+                num = "".join(ch for ch in line.split(":", 1)[-1] if ch.isdigit())
+                return int(num) if num else None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                with open(self.path) as f:
+                    mhz = self.parse(f.read())
+                if mhz:
+                    self.samples.append(mhz)
+            except OSError:
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.path:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"median_mhz": xs[len(xs) // 2], "min_mhz": xs[0], "max_mhz": xs[-1],
+                "samples": len(xs), "source": "pp_dpm_sclk, sampled every 2 ms"}
+
+
+def prefill_counter_record(kernel_sha):
+    """Per-leg counter figures of the committed prefill summary, if it was taken on the
+    current prefill sources; otherwise None."""
+    try:
+        with open(PREFILL_COUNTERS_JSON) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return c if c.get("source_sha") == kernel_sha else None
+
+
+def prefill_roofline(leg, tflops, flop, median_us, counters):
+    """The roofline object of one prefill leg: achieved algorithmic TFLOP/s of the median
+    call against the dense bf16 MFMA peak, with MFMA-busy and HBM traffic from the
+    counter summary when it matches the sources."""
+    rec = (counters or {}).get("legs", {}).get(leg, {})
+    return {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": round(tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": rec.get("fetch_bytes_per_call"), "mfma_busy": rec.get("mfma_busy"),
+            "valu_mfma_coexec": rec.get("coexec_of_mfma_busy"),
+            "counter_clock_mhz": rec.get("clock_mhz"),
+            "algorithmic_flop_per_launch": int(flop), "avg_launch_us": round(median_us, 2),
+            "kernel_source_sha": kernel_source_sha(PREFILL_SOURCES)}
 
 
 def i32(a, dev):
@@ -215,18 +313,19 @@ def bench_decode(dev, steps, warmup, graph=True):
     for _ in range(max(1, warmup // 3)):
         three.replay()
     torch.cuda.synchronize()
-    t0.record()
-    for _ in range(steps // 3):
-        three.replay()
-    for i in range(steps % 3):
-        single[i].replay()
-    t1.record()
-    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        t0.record()
+        for _ in range(steps // 3):
+            three.replay()
+        for i in range(steps % 3):
+            single[i].replay()
+        t1.record()
+        torch.cuda.synchronize()
     graph_ms_step = t0.elapsed_time(t1) / steps
     log(f"[decode C2, graph replay] step {graph_ms_step*1e3:.1f} us over {steps} steps")
     return dict(case=case, ms_step=ms_step, store_ms=store_ms, dec_ms=dec_ms, dec_bytes=dec_bytes,
                 st_bytes=st_bytes, workspace_bytes=need, dec_stats=dec_stats, store_stats=store_stats,
-                graph_ms_step=graph_ms_step)
+                graph_ms_step=graph_ms_step, engine_clock=clk.summary())
 
 
 def prefill_inputs(dev, which):
@@ -283,12 +382,13 @@ def bench_prefill(dev, which, steps, warmup, settle_s=1.5):
     # (the engine clock settles under the sustained load): time a few calls right away
     # ("cold"), keep the matrix cores busy for settle_s, then time the steady state.
     cold = stats_us([e[1].elapsed_time(e[2]) for e in timed(10)])
-    t_end = time.perf_counter() + settle_s
-    while time.perf_counter() < t_end:
-        for _ in range(20):
-            step()
-        torch.cuda.synchronize()
-    evs = timed(steps)
+    with ClockSampler() as clk:          # over the settling and the timed calls
+        t_end = time.perf_counter() + settle_s
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+        evs = timed(steps)
     st_stats = stats_us([e[0].elapsed_time(e[1]) for e in evs])
     pf_stats = stats_us([e[1].elapsed_time(e[2]) for e in evs])
     # The median call: a rare stall of tens of milliseconds inside one timed interval (seen
@@ -305,7 +405,10 @@ def bench_prefill(dev, which, steps, warmup, settle_s=1.5):
             "tflops": round(tflops, 2), "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "flop": flops, "prefill_call": pf_stats, "cold_prefill_call": cold,
             "settle_s": settle_s, "store_us": round(store_ms * 1e3, 2), "store_call": st_stats,
-            "store_gbs": round(st_bytes / store_ms / 1e6, 1)}
+            "store_gbs": round(st_bytes / store_ms / 1e6, 1),
+            "engine_clock": clk.summary(),
+            "roofline": prefill_roofline(which, tflops, flops, pf_ms * 1e3,
+                                         prefill_counter_record(kernel_source_sha(PREFILL_SOURCES)))}
 
 
 def bench_varlen_prefill(dev, steps, warmup, settle_s=1.5):
@@ -502,7 +605,51 @@ def bench_add_rms_norm(dev, which, steps, warmup):
             "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def bench_c5(dev, kind, reps, warmup):
+def blas_threads():
+    try:
+        import threadpoolctl
+        blas = [p["num_threads"] for p in threadpoolctl.threadpool_info() if p["user_api"] == "blas"]
+        return max(blas) if blas else 1
+    except Exception:  # noqa: BLE001
+        return 1
+
+
+def cpu_baseline_layer(layer, lens, kind):
+    """The float64 oracle's decode (decode_ref) of one full layer of a long-context
+    workload on the host cores: the layer's q, pools and table copied to the host (timed
+    apart), then decode_ref over every sequence.  Reported per layer and, extrapolated,
+    for the 36 layers."""
+    import numpy as np
+    import torch
+    from oracle import ref
+    from paged_kv_cache_258_amd import accounting as acc
+    from paged_kv_cache_258_amd import workloads as wl
+
+    def bits(t):
+        return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    q, kc, vc, table = layer
+    sh = wl.QWEN3_8B
+    t = time.perf_counter()
+    qh, kh, vh = bits(q), bits(kc), bits(vc)
+    t_copy = time.perf_counter() - t
+    t = time.perf_counter()
+    ref.decode_ref(qh, kh, vh, lens, table, sh.scale, elem="bf16")
+    per = time.perf_counter() - t
+    nbytes = acc.decode_bytes(lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                              sh.elem_bytes)
+    log(f"[cpu oracle C5{kind}] layer 0: {per:.2f} s ({len(lens)} seqs, sum ctx {int(lens.sum())}), "
+        f"D2H copy {t_copy:.2f}s")
+    return {"workload": f"C5{kind}", "value": round(nbytes / per / 1e9, 4), "unit": "GB/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"full layer 0 of C5{kind} ({len(lens)} seqs, sum ctx {int(lens.sum())}): "
+                      f"decode_ref in numpy float64, 1 run",
+            "per_layer_s": round(per, 3), "all_layers_s_extrapolated": round(per * wl.NUM_LAYERS, 2),
+            "d2h_copy_s": round(t_copy, 2), "cpu_model": cpu_model(),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def bench_c5(dev, kind, reps, warmup, cpu=False):
     """C5a / C5b: layer-by-layer decode over all 36 layers' pools (no store: the pools
     are pre-filled).  Every layer has its own pools, so no layer finds another's K/V in
     cache.  If the 36 layers do not fit in free device memory minus an 8 GB margin, the
@@ -570,7 +717,10 @@ def bench_c5(dev, kind, reps, warmup):
            "all_layers_ms": round(per_layer_ms * wl.NUM_LAYERS, 3),
            "decode_bytes_per_layer": int(nbytes), "gbs": round(gbs, 1),
            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-    del mld, tables, outs, ws
+    del tables, outs, ws
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_layer(mld.layers[0], lens, kind)
+    del mld
     torch.cuda.empty_cache()
     return res
 
@@ -601,18 +751,13 @@ def cpu_baseline(case, budget_s=10.0):
     nbytes = acc.decode_bytes(case.context_lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
                               sh.block_size, sh.elem_bytes) + \
         acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
-    try:
-        import threadpoolctl
-        blas = [p["num_threads"] for p in threadpoolctl.threadpool_info() if p["user_api"] == "blas"]
-        threads = max(blas) if blas else 1
-    except Exception:  # noqa: BLE001
-        threads = 1
     log(f"[cpu oracle] {per:.3f} s per C2 step ({runs} runs), D2H copy {t_copy:.2f}s")
-    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": threads,
+    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": blas_threads(),
             "kind": "oracle",
             "sample": f"full C2 batch (64 seqs, sum ctx {int(case.context_lens.sum())}): "
                       f"store_ref + decode_ref in numpy float64, {runs} run(s), "
-                      f"{per:.2f} s each; host affinity {len(os.sched_getaffinity(0))} cpus"}
+                      f"{per:.2f} s each; host affinity {len(os.sched_getaffinity(0))} cpus",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def traffic_from_counters(kernel_sha):
@@ -844,6 +989,26 @@ def summarize_prefill_counters(paths):
     with open(PREFILL_COUNTERS, "w") as f:
         f.write(text)
     print(text)
+    # the figures bench.py's prefill roofline blocks quote, behind the same source check
+    legs = {}
+    for leg in ("C3", "C4"):
+        def val(f):
+            try:
+                return f()
+            except (TypeError, ZeroDivisionError, KeyError):
+                return None
+        legs[leg] = {
+            "duration_us": val(lambda: round(d(leg), 2)),
+            "clock_mhz": val(lambda: round(gui(leg) / d(leg))),
+            "mfma_busy": val(lambda: round(m(leg, "SQ_VALU_MFMA_BUSY_CYCLES") / (simds * gui(leg)), 4)),
+            "coexec_of_mfma_busy": val(lambda: round(m(leg, "SQ_VALU_MFMA_COEXEC_CYCLES") /
+                                                     m(leg, "SQ_VALU_MFMA_BUSY_CYCLES"), 4)),
+            "fetch_bytes_per_call": val(lambda: int(m(leg, "FETCH_SIZE") * 1024 * factor)),
+            "lds_bank_conflict_share": val(lambda: round(m(leg, "SQ_LDS_BANK_CONFLICT") /
+                                                         m(leg, "SQ_LDS_IDX_ACTIVE"), 4)),
+        }
+    with open(PREFILL_COUNTERS_JSON, "w") as f:
+        json.dump({"source_sha": kernel_source_sha(PREFILL_SOURCES), "legs": legs}, f, indent=1)
 
 
 PREFILL_COUNTER_GROUPS = [
@@ -916,7 +1081,7 @@ def main():
     long_decode = []
     if not args.no_c5:
         for kind in ("a", "b"):
-            long_decode.append(bench_c5(dev, kind, 5, 1))
+            long_decode.append(bench_c5(dev, kind, 5, 1, cpu=not args.no_cpu))
     cpu = None if args.no_cpu else cpu_baseline(d["case"])
     block_manager = bench_block_manager()
 
@@ -965,6 +1130,10 @@ def main():
         "eager_step": {"ms_per_step": round(d["ms_step"], 5),
                        "value": round(step_bytes / d["ms_step"] / 1e6, 1), "unit": "GB/s"},
         "peaks": device_peaks(props),
+        "engine_clock": {"decode_graph_steps": d.get("engine_clock"),
+                         "prefill_C3": prefill[0].get("engine_clock") if prefill else None,
+                         "prefill_C4": prefill[1].get("engine_clock") if len(prefill) > 1 else None},
+        "host": {"cpu_model": cpu_model(), "cpus": len(os.sched_getaffinity(0))},
         "store": {"avg_launch_us": round(d["store_ms"] * 1e3, 2), "call": d["store_stats"],
                   "gbs": round(d["st_bytes"] / d["store_ms"] / 1e6, 1)},
         "prefill": prefill,

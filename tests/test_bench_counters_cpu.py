@@ -62,6 +62,7 @@ def test_decode_summary_calibrates_and_sums_per_call(tmp_path, monkeypatch):
 def test_prefill_summary_derived_figures(tmp_path, monkeypatch):
     out = tmp_path / "prefill.md"
     monkeypatch.setattr(bench, "PREFILL_COUNTERS", str(out))
+    monkeypatch.setattr(bench, "PREFILL_COUNTERS_JSON", str(tmp_path / "prefill.json"))
     c3, c4 = bench.PREFILL_GRIDS["C3"], bench.PREFILL_GRIDS["C4"]
     k = "void nkv::prefill_bf16_kernel<128, 4, 8>(...)"
     dur_ns = {c3: 400_000, c4: 200_000}               # 400 us and 200 us per dispatch
@@ -109,3 +110,51 @@ def test_prefill_summary_derived_figures(tmp_path, monkeypatch):
     tf3 = bench.PREFILL_FLOP["C3"] / 400.0 / 1e6
     assert row("TFLOP/s in the counted dispatches")[0] == f"{tf3:,.1f}"
     assert row("duration_us") == ("400.00", "200.00")
+
+
+def test_prefill_summary_writes_the_roofline_record(tmp_path, monkeypatch):
+    # the JSON record beside the markdown: per-leg MFMA busy, co-execution share, clock and
+    # calibrated FETCH bytes, tagged with the prefill sources' sha
+    monkeypatch.setattr(bench, "PREFILL_COUNTERS", str(tmp_path / "prefill.md"))
+    monkeypatch.setattr(bench, "PREFILL_COUNTERS_JSON", str(tmp_path / "prefill.json"))
+    c3 = bench.PREFILL_GRIDS["C3"]
+    k = "void nkv::prefill_bf16_kernel<128, 4, 8>(...)"
+    passes = [[], [], [(1, "void at::native::neg_kernel", 1, "FETCH_SIZE", bench.COPY_BYTES / 4 / 1024, 0, 1)]]
+    for did in range(2, 6):
+        t0, t1 = 1_000_000 * did, 1_000_000 * did + 500_000          # 500 us
+        passes[0] += [(did, k, c3, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1_000_000 * 0.5, t0, t1),
+                      (did, k, c3, "GRBM_GUI_ACTIVE", 8 * 1_000_000, t0, t1),
+                      (did, k, c3, "SQ_VALU_MFMA_COEXEC_CYCLES", 1024 * 1_000_000 * 0.1, t0, t1)]
+        passes[1] += [(did, k, c3, "SQ_LDS_BANK_CONFLICT", 10.0, t0, t1),
+                      (did, k, c3, "SQ_LDS_IDX_ACTIVE", 40.0, t0, t1)]
+        passes[2] += [(did, k, c3, "FETCH_SIZE", 1000.0, t0, t1)]
+    paths = []
+    for i, rows in enumerate(passes):
+        d = tmp_path / f"p{i}"
+        d.mkdir()
+        write_csv(d / "pass_counter_collection.csv", rows)
+        write_agent(d / "pass_agent_info.csv")
+        paths.append(str(d / "pass_counter_collection.csv"))
+    bench.summarize_prefill_counters(paths)
+    rec = json.loads((tmp_path / "prefill.json").read_text())
+    assert rec["source_sha"] == bench.kernel_source_sha(bench.PREFILL_SOURCES)
+    c = rec["legs"]["C3"]
+    assert c["duration_us"] == 500.0 and c["clock_mhz"] == 2000
+    assert c["mfma_busy"] == 0.5 and c["coexec_of_mfma_busy"] == 0.2
+    assert c["lds_bank_conflict_share"] == 0.25
+    assert c["fetch_bytes_per_call"] == 1000 * 1024 * 4          # the copy reads as a quarter
+    assert rec["legs"]["C4"]["mfma_busy"] is None
+    # the bench reads it back only for the same sources
+    monkeypatch.setattr(bench, "PREFILL_COUNTERS_JSON", str(tmp_path / "prefill.json"))
+    assert bench.prefill_counter_record(rec["source_sha"]) == rec
+    assert bench.prefill_counter_record("0" * 16) is None
+    r = bench.prefill_roofline("C3", 1000.0, 2.75e11, 275.0, rec)
+    assert r["frac"] == 0.4 and r["mfma_busy"] == 0.5 and r["traffic"] == 1000 * 1024 * 4
+    assert bench.prefill_roofline("C3", 1000.0, 2.75e11, 275.0, None)["traffic"] is None
+
+
+def test_clock_sampler_reads_the_current_level():
+    text = "0: 500Mhz\n1: 2400Mhz\nS: 2013Mhz *\n"
+    assert bench.ClockSampler.parse(text) == 2013
+    assert bench.ClockSampler.parse("0: 500Mhz *\n1: 2400Mhz\n") == 500
+    assert bench.ClockSampler.parse("0: 500Mhz\n") is None
