@@ -57,6 +57,17 @@ int num_cus() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The value of an enum argument as the int the caller passed.  Across the C ABI any int
+// may arrive; reading one outside the enumerators' range through the C++ enum type would
+// be undefined behaviour, so it is read as an int and compared with the enumerators.
+template <class E>
+int abi_int(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 int ilog2_exact(int x) {
   if (x <= 0 || (x & (x - 1)) != 0) return -1;
   int r = 0;
@@ -64,13 +75,13 @@ int ilog2_exact(int x) {
   return r;
 }
 
-int elem_bytes(nkv_dtype_t dt) { return dt == NKV_BF16 ? 2 : 4; }
+int elem_bytes(int dt) { return dt == NKV_BF16 ? 2 : 4; }
 
 // Checks shared by prefill and decode; fills the common launch descriptor.
 nkv_status_t check_paged(const void* k_cache, const void* v_cache, const int32_t* block_table,
                          int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
-                         int32_t block_size, float softmax_scale, nkv_dtype_t dtype,
+                         int32_t block_size, float softmax_scale, int dtype,
                          nkv::PagedArgs* pa) {
   if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (num_seqs < 0) return fail(NKV_ERR_INVALID_ARG, "num_seqs < 0");
@@ -159,8 +170,8 @@ nkv_status_t clear_error() { return ok(); }
 
 NKV_EXPORT int nkv_abi_version(void) { return NKV_ABI_VERSION; }
 
-NKV_EXPORT const char* nkv_status_string(nkv_status_t s) {
-  switch (s) {
+NKV_EXPORT const char* nkv_status_string(nkv_status_t status) {
+  switch (abi_int(status)) {
     case NKV_OK: return "NKV_OK";
     case NKV_ERR_INVALID_ARG: return "NKV_ERR_INVALID_ARG";
     case NKV_ERR_UNSUPPORTED: return "NKV_ERR_UNSUPPORTED";
@@ -179,7 +190,8 @@ NKV_EXPORT nkv_status_t nkv_store_kvcache(const void* key, int64_t key_row_strid
                                           const int32_t* slot_mapping, int32_t num_tokens,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t num_blocks, int32_t block_size,
-                                          nkv_dtype_t dtype, hipStream_t stream) {
+                                          nkv_dtype_t dtype_arg, hipStream_t stream) {
+  const int dtype = abi_int(dtype_arg);
   if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (num_tokens < 0) return fail(NKV_ERR_INVALID_ARG, "num_tokens < 0");
   if (num_kv_heads <= 0 || head_dim <= 0) return fail(NKV_ERR_INVALID_ARG, "num_kv_heads and head_dim must be positive");
@@ -216,7 +228,8 @@ NKV_EXPORT nkv_status_t nkv_qk_norm_rope_store(
     const void* k_norm_weight, const float* cos_sin_cache, int32_t max_position, float eps,
     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, void* q_out, void* k_cache, void* v_cache, int32_t num_blocks,
-    int32_t block_size, nkv_dtype_t dtype, hipStream_t stream) {
+    int32_t block_size, nkv_dtype_t dtype_arg, hipStream_t stream) {
+  const int dtype = abi_int(dtype_arg);
   if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (dtype != NKV_BF16) return fail(NKV_ERR_UNSUPPORTED, "q/k norm + rotary is implemented for bf16 only");
   if (num_tokens < 0) return fail(NKV_ERR_INVALID_ARG, "num_tokens < 0");
@@ -255,8 +268,9 @@ NKV_EXPORT nkv_status_t nkv_qk_norm_rope_store(
 
 NKV_EXPORT nkv_status_t nkv_add_rms_norm(const void* x, const void* residual, const void* weight,
                                          float eps, int32_t num_tokens, int32_t hidden_size,
-                                         void* out, void* residual_out, nkv_dtype_t dtype,
+                                         void* out, void* residual_out, nkv_dtype_t dtype_arg,
                                          hipStream_t stream) {
+  const int dtype = abi_int(dtype_arg);
   if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (dtype != NKV_BF16) return fail(NKV_ERR_UNSUPPORTED, "residual add + RMSNorm is implemented for bf16 only");
   if (num_tokens < 0) return fail(NKV_ERR_INVALID_ARG, "num_tokens < 0");
@@ -290,8 +304,9 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_prefill(
     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_table,
     int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
     int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t num_blocks, int32_t block_size, float softmax_scale, nkv_dtype_t dtype, void* out,
+    int32_t num_blocks, int32_t block_size, float softmax_scale, nkv_dtype_t dtype_arg, void* out,
     hipStream_t stream) {
+  const int dtype = abi_int(dtype_arg);
   nkv::PrefillArgs a{};
   nkv_status_t st = check_paged(k_cache, v_cache, block_table, max_blocks_per_seq, num_seqs,
                                 num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
@@ -331,8 +346,9 @@ NKV_EXPORT nkv_status_t nkv_attn_varlen_prefill(
     const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride, const void* v,
     int64_t v_row_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
     int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t head_dim, float softmax_scale, nkv_dtype_t dtype, void* out,
+    int32_t num_kv_heads, int32_t head_dim, float softmax_scale, nkv_dtype_t dtype_arg, void* out,
     hipStream_t stream) {
+  const int dtype = abi_int(dtype_arg);
   if (dtype != NKV_F32 && dtype != NKV_BF16) return fail(NKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(NKV_ERR_INVALID_ARG, "negative size");
@@ -442,7 +458,7 @@ nkv_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache
                          const int32_t* context_lens, const int32_t* block_table,
                          int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
-                         int32_t block_size, float softmax_scale, nkv_dtype_t dtype, void* out,
+                         int32_t block_size, float softmax_scale, int dtype, void* out,
                          void* workspace, size_t workspace_bytes, bool scratch, hipStream_t stream) {
   nkv::DecodeArgs a{};
   nkv_status_t st = check_paged(k_cache, v_cache, block_table, max_blocks_per_seq, num_seqs,
@@ -489,8 +505,9 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_decode(
     const void* q, const void* k_cache, const void* v_cache, const int32_t* context_lens,
     const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
-    float softmax_scale, nkv_dtype_t dtype, void* out, void* workspace, size_t workspace_bytes,
+    float softmax_scale, nkv_dtype_t dtype_arg, void* out, void* workspace, size_t workspace_bytes,
     hipStream_t stream) {
+  const int dtype = abi_int(dtype_arg);
   return decode_impl(q, k_cache, v_cache, context_lens, block_table, max_blocks_per_seq, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, softmax_scale, dtype,
                      out, workspace, workspace_bytes, false, stream);
@@ -500,7 +517,8 @@ NKV_EXPORT nkv_status_t nkv_paged_attn_decode_noalloc(
     const void* q, const void* k_cache, const void* v_cache, const int32_t* context_lens,
     const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
-    float softmax_scale, nkv_dtype_t dtype, void* out, hipStream_t stream) {
+    float softmax_scale, nkv_dtype_t dtype_arg, void* out, hipStream_t stream) {
+  const int dtype = abi_int(dtype_arg);
   return decode_impl(q, k_cache, v_cache, context_lens, block_table, max_blocks_per_seq, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, softmax_scale, dtype,
                      out, nullptr, 0, true, stream);
