@@ -28,7 +28,8 @@ full layer 0 (C5a: 4 sequences, C5b: all 256), per layer and x36 "extrapolated".
 engine_clock = the GPU engine clock the driver reports (pp_dpm_sclk), sampled every 2 ms
 while the decode graph steps are timed and while each prefill leg settles and is timed.
 prefill[i].roofline = the leg's algorithmic TFLOP/s against the dense bf16 MFMA peak, with
-MFMA busy, VALU-MFMA co-execution and HBM traffic (FETCH_SIZE, calibrated) from
+MFMA busy, VALU-MFMA co-execution and the bytes read from beyond L2 (FETCH_SIZE, calibrated,
+MALL hits included: an upper bound on HBM reads) from
 profiles/prefill_c3_c4_counters.json when it was taken on the current prefill sources.
 decode_call / prefill_call / store_call = mean, median and minimum of the per-call event times; the
 prefill legs' headline times (the prefill and the store before it) are the median calls.
@@ -215,7 +216,7 @@ def prefill_counter_record(kernel_sha):
 
 def prefill_roofline(leg, tflops, flop, median_us, counters):
     """The roofline object of one prefill leg: achieved algorithmic TFLOP/s of the median
-    call against the dense bf16 MFMA peak, with MFMA-busy and HBM traffic from the
+    call against the dense bf16 MFMA peak, with MFMA-busy and the bytes read from beyond L2 from the
     counter summary when it matches the sources."""
     rec = (counters or {}).get("legs", {}).get(leg, {})
     return {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": round(tflops, 1),
@@ -979,7 +980,8 @@ def summarize_prefill_counters(paths):
         lambda leg: f"{m(leg, 'SQ_WAIT_INST_LDS') / m(leg, 'SQ_WAIT_INST_ANY'):.3f}")
     row("L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))",
         lambda leg: f"{m(leg, 'TCC_HIT_sum') / (m(leg, 'TCC_HIT_sum') + m(leg, 'TCC_MISS_sum')):.3f}")
-    row(f"HBM-side read bytes (FETCH_SIZE x {factor:.3f})" if factor else "HBM-side read bytes",
+    row(f"bytes read from beyond L2, MALL hits included (FETCH_SIZE x {factor:.3f})" if factor
+        else "bytes read from beyond L2, MALL hits included",
         lambda leg: f"{m(leg, 'FETCH_SIZE') * 1024 * factor / 1e6:,.1f} MB")
     row("... / bytes the leg must read once (q, K/V, tables)",
         lambda leg: f"{m(leg, 'FETCH_SIZE') * 1024 * factor / PREFILL_UNIQUE_READ[leg]:.2f}")

@@ -106,7 +106,7 @@ def test_prefill_summary_derived_figures(tmp_path, monkeypatch):
     assert row("VALU-MFMA co-execution / MFMA busy") == ("0.250", "0.250")
     assert row("LDS bank conflicts / LDS active") == ("0.250", "0.250")
     assert row("L2 hit rate") == ("0.600", "0.600")
-    assert row("HBM-side read bytes") == ("204.8 MB", "204.8 MB")
+    assert row("bytes read from beyond L2") == ("204.8 MB", "204.8 MB")
     tf3 = bench.PREFILL_FLOP["C3"] / 400.0 / 1e6
     assert row("TFLOP/s in the counted dispatches")[0] == f"{tf3:,.1f}"
     assert row("duration_us") == ("400.00", "200.00")
