@@ -12,10 +12,10 @@
 //   waves (two per SIMD) holds the G query heads of one KV head; each wave owns 32
 //   queries of one head, two 16-query MFMA column blocks.  K/V tiles of 128 keys are
 //   gathered through the block table into a double-buffered LDS stage shared by all
-//   waves: K and V rows are copied HBM -> LDS directly (global_load_lds, chunk c of row
-//   t at c ^ t to spread banks).  K fragments are 16-byte LDS reads; V^T fragments come
-//   from the transposing LDS read (ds_read_b64_tr_b16), two per fragment, in the key
-//   order of the P^T operand.  The next tile's copies are in flight while the current
+//   waves: K and V rows are copied HBM -> LDS directly, by waves 0-3 only (global_load_lds,
+//   chunk c of row t at c ^ t to spread banks).  K fragments are 16-byte LDS reads; V^T
+//   fragments come from the transposing LDS read (ds_read_b64_tr_b16), two per fragment,
+//   in the key order of the P^T operand.  The next tile's copies are in flight while the current
 //   tile is computed.
 //   Scores are computed transposed, S^T = K Q^T, in 16x16 blocks: a lane holds 4 keys of
 //   one query per block, so the max of a query spans four lanes and its row sum stays in
@@ -72,10 +72,11 @@ struct PfGeom {
   static constexpr int CPR = D / 8;             // 16-byte chunks per K row
   static constexpr int K_BYTES = kBK * D * 2;   // one K (or V) tile
   static constexpr int STAGE = 2 * K_BYTES;     // K rows, then V rows, same layout
-  static constexpr int K_DMA = K_BYTES / 1024 / NW;   // copy instructions per wave per tile (K or V)
+  static constexpr int CW = NW / 2;             // waves that issue the K/V copies (the first half)
+  static constexpr int K_DMA = K_BYTES / 1024 / CW;   // copy instructions per copying wave per tile (K or V)
   static constexpr int OROW = D * 2 + 16;             // output staging row stride (bytes)
   static_assert(G >= 1 && G <= NW && NW % G == 0, "GQA group must divide the waves");
-  static_assert(K_DMA >= 1 && K_BYTES % (1024 * NW) == 0, "K tile must split over the waves");
+  static_assert(K_DMA >= 1 && K_BYTES % (1024 * CW) == 0, "K tile must split over the copying waves");
   static constexpr int SMEM = kStages * STAGE > NW * WQ * OROW ? kStages * STAGE : NW * WQ * OROW;
 };
 
@@ -141,7 +142,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     }
   }
 
-  // ---- copies: block ids two tiles ahead (LDS), K rows by DMA, V through registers ----
+  // ---- copies: block ids two tiles ahead (LDS), K and V rows by DMA ----
   auto issue_ids = [&](int t) {                       // wave 0: ids of tile t -> s_ids[t % 3]
     if (paged && wave == 0 && lane < ids_per_tile) {
       const int blk = min(((t * kBK) >> log2_bs) + lane, last_blk);
@@ -152,10 +153,17 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     const int64_t phys = s_ids[t % 3][((key - t * kBK) >> log2_bs) & (kMaxIds - 1)];
     return ((phys << log2_bs) + (key & bs_mask)) * row_elems;
   };
+  // The K/V copies of a tile are issued by waves 0..NW/2-1 only.  A wave waits at each copy
+  // instruction until the CU takes it, slowly for a whole tile's worth: issued by all
+  // waves at the top of a tile they held both waves of every SIMD (about 1500 cycles per
+  // tile); issued by one wave of each SIMD pair (w, w + NW/2), the partner computes
+  // meanwhile (C3 loop 3.80 -> 3.49 us per tile).
+  const bool copier = wave < Geo::CW;
+  const int cwave = wave % Geo::CW;
   int k_row[Geo::K_DMA], k_elem[Geo::K_DMA];
 #pragma unroll
   for (int j = 0; j < Geo::K_DMA; ++j) {
-    const int s = (wave * Geo::K_DMA + j) * 64 + lane;   // LDS slot this lane fills
+    const int s = (cwave * Geo::K_DMA + j) * 64 + lane;  // LDS slot this lane fills
     k_row[j] = s / CPR;
     k_elem[j] = ((s % CPR) ^ (k_row[j] & (CPR - 1))) * 8;
   }
@@ -187,20 +195,21 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       if (rmax >= kBK - 1) {
 #pragma unroll
         for (int j = 0; j < Geo::K_DMA; ++j)
-          load_lds16_s(tb, region == 0 ? koff[j] : voff[j], sk + (wave * Geo::K_DMA + j) * 1024);
+          load_lds16_s(tb, region == 0 ? koff[j] : voff[j], sk + (cwave * Geo::K_DMA + j) * 1024);
       } else {
 #pragma unroll
         for (int j = 0; j < Geo::K_DMA; ++j)
           load_lds16_s(tb, uint32_t((min(k_row[j], rmax) * stride + k_elem[j]) * 2),
-                       sk + (wave * Geo::K_DMA + j) * 1024);
+                       sk + (cwave * Geo::K_DMA + j) * 1024);
       }
       return;
     }
 #pragma unroll
     for (int j = 0; j < Geo::K_DMA; ++j)
-      load_lds16(tb + min(k_row[j], rmax) * stride + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
+      load_lds16(tb + min(k_row[j], rmax) * stride + k_elem[j], sk + (cwave * Geo::K_DMA + j) * 1024);
   };
   auto issue_rows = [&](int t, const uint16_t* base, int64_t stride, int region) {
+    if (!copier) return;
     if (tile_in_block) {
       issue_rows_at(t, tile_base(t, base, stride), stride, region);
     } else {
@@ -209,7 +218,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
 #pragma unroll
       for (int j = 0; j < Geo::K_DMA; ++j) {
         const int key = t * kBK + min(k_row[j], rmax);
-        load_lds16(base + row_off(t, key) + k_elem[j], sk + (wave * Geo::K_DMA + j) * 1024);
+        load_lds16(base + row_off(t, key) + k_elem[j], sk + (cwave * Geo::K_DMA + j) * 1024);
       }
     }
   };
@@ -353,8 +362,10 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       k0b = kbase + (phys0 << log2_bs) * k_stride;
       v0b = vbase + (phys0 << log2_bs) * v_stride;
     }
-    issue_rows_at(0, k0b, k_stride, 0);
-    issue_rows_at(0, v0b, v_stride, Geo::K_BYTES);
+    if (copier) {
+      issue_rows_at(0, k0b, k_stride, 0);
+      issue_rows_at(0, v0b, v_stride, Geo::K_BYTES);
+    }
     if (ntiles > 1) issue_ids(1);
     if (ntiles > 2) issue_ids(2);
   } else {
