@@ -13,7 +13,7 @@
 //   queries of one head, two 16-query MFMA column blocks.  K/V tiles of 128 keys are
 //   gathered through the block table into a double-buffered LDS stage shared by all
 //   waves: K and V rows are copied HBM -> LDS directly, by waves 0-3 only (global_load_lds,
-//   chunk c of row t at c ^ t to spread banks).  K fragments are 16-byte LDS reads; V^T
+//   chunk c of row t at c ^ kv_swz(t), free of bank conflicts for both kinds of read).  K fragments are 16-byte LDS reads; V^T
 //   fragments come from the transposing LDS read (ds_read_b64_tr_b16), two per fragment,
 //   in the key order of the P^T operand.  The next tile's copies are in flight while the current
 //   tile is computed.
@@ -55,6 +55,23 @@ constexpr float kLazyBound = 256.0f;    // largest weight kept before rescaling 
 constexpr int kMaxIds = kBK / 16;       // block ids per tile (block_size >= 16)
 constexpr int kLog2BK = kBK == 128 ? 7 : 6;
 static_assert(kBK == 64 || kBK == 128, "64- or 128-key tiles");
+
+// Swizzle of the 16-byte chunks of a K/V tile row in LDS: logical chunk c of row t sits at
+// c ^ kv_swz(t).  It must keep two read patterns free of bank conflicts: the K fragment
+// reads (ds_read_b128, 16 consecutive rows at one logical chunk per 16 lanes) and the V^T
+// transposing reads (ds_read_b64_tr_b16, 4 consecutive rows x 2 adjacent chunks per 16
+// lanes).  Plain c ^ (t % 16) leaves the transposing reads 2 extra cycles each (a third
+// of all LDS cycles in conflict); the map below was found by counting
+// SQ_LDS_BANK_CONFLICT over candidate maps in a read-only probe and is conflict-free for
+// both (bits of the result, high to low: t0, t2 ^ t3, t1 ^ t2, t3).  Rows of 64 dims keep
+// c ^ (t % 8).
+template <int CPR>
+__device__ __forceinline__ int kv_swz(int t) {
+  if constexpr (CPR == 16)
+    return ((t & 1) << 3) | ((((t >> 2) ^ (t >> 3)) & 1) << 2) | ((((t >> 1) ^ (t >> 2)) & 1) << 1) | ((t >> 3) & 1);
+  else
+    return t & (CPR - 1);
+}
 
 // Eight waves of 32 queries run two per SIMD inside one workgroup.  Four waves with
 // 64-key tiles (NKV_PREFILL_NW=4, NKV_PREFILL_BK=64: 64 KB of LDS) let two workgroups
@@ -165,7 +182,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   for (int j = 0; j < Geo::K_DMA; ++j) {
     const int s = (cwave * Geo::K_DMA + j) * 64 + lane;  // LDS slot this lane fills
     k_row[j] = s / CPR;
-    k_elem[j] = ((s % CPR) ^ (k_row[j] & (CPR - 1))) * 8;
+    k_elem[j] = ((s % CPR) ^ kv_swz<CPR>(k_row[j])) * 8;
   }
   // With block_size >= kBK a tile lies inside one physical block: its base is uniform
   // (one LDS read, scalar math) and each lane adds only row * stride.  Contiguous K/V is
@@ -234,13 +251,16 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // Fragments of the 32-key half `kb` of the tile in stage `st`: K rows of its two
   // 16-key blocks (A operand of S^T = K Q^T) and V^T rows of its 16-dim tiles (A operand
   // of O^T += V^T P^T), read ahead of their MFMAs.
+  // A lane's fragment rows are a multiple of 16 plus col (K) or v_row (V^T), so their
+  // swizzle is fixed per lane.
+  const int swz_k = kv_swz<CPR>(col);
   auto read_k = [&](const uint8_t* st, int kb, bf16x8_t (&kf)[2][KS]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int t = kb * 32 + 16 * i + col;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kf[i][ks] = *reinterpret_cast<const bf16x8_t*>(st + (t * CPR + ((4 * ks + quad) ^ (t & (CPR - 1)))) * 16);
+        kf[i][ks] = *reinterpret_cast<const bf16x8_t*>(st + (t * CPR + ((4 * ks + quad) ^ swz_k)) * 16);
     }
   };
   // V^T fragments by the transposing LDS read: in each 16-lane quarter, lane col addresses
@@ -248,6 +268,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // it dim col of the quarter's 4 rows.  Two reads (key blocks 0 and 1) make the 8 keys
   // 4*quad + r and 16 + 4*quad + r that the lane's P^T operand holds, in that order.
   const int v_row = 4 * quad + (col >> 2), v_dim = 4 * (col & 3);
+  const int swz_v = kv_swz<CPR>(v_row);
   auto read_v = [&](const uint8_t* st, int kb, bf16x8_t (&vf)[DT]) {
     const uint8_t* sv = st + Geo::K_BYTES;
 #pragma unroll
@@ -256,7 +277,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int t = kb * 32 + 16 * i + v_row, d = dt * 16 + v_dim;
-        const uint8_t* a = sv + (t * CPR + ((d >> 3) ^ (t & (CPR - 1)))) * 16 + (d & 7) * 2;
+        const uint8_t* a = sv + (t * CPR + ((d >> 3) ^ swz_v)) * 16 + (d & 7) * 2;
         h[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
       }
       vf[dt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
