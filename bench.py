@@ -18,7 +18,10 @@ one per rotated pool copy, plus single-step graphs for the remainder, so exactly
 steps are timed; ms_per_step is the event time per step).  eager_step gives the same
 step launched call by call.
 roofline = the decode call (stream-K kernel + its fixup kernel) timed with HIP events on
-the stream it runs on: algorithmic decode bytes / average duration vs 8 TB/s.
+the stream it runs on: algorithmic decode bytes / average duration vs 8 TB/s.  The average
+duration is that of `steps` decode calls launched back to back (over the same 3 rotated pool
+copies) between one event pair; per_call_event_us keeps the mean of the per-call event pairs
+of the eager steps, which add a few microseconds of event overhead to each ~100-us call.
 traffic = HBM bytes per decode call measured by rocprofv3 counters (FETCH_SIZE and
 WRITE_SIZE, calibrated on a plain copy of known size), read from
 profiles/decode_c2_counters.json when it was taken on the current decode sources.
@@ -31,8 +34,12 @@ prefill[i].roofline = the leg's algorithmic TFLOP/s against the dense bf16 MFMA 
 MFMA busy, VALU-MFMA co-execution and the bytes read from beyond L2 (FETCH_SIZE, calibrated,
 MALL hits included: an upper bound on HBM reads) from
 profiles/prefill_c3_c4_counters.json when it was taken on the current prefill sources.
-decode_call / prefill_call / store_call = mean, median and minimum of the per-call event times; the
-prefill legs' headline times (the prefill and the store before it) are the median calls.
+decode_call / prefill_call / store_call = mean, median and minimum of the per-call event times;
+the prefill legs' headline times (the prefill and the store before it) are the median calls.
+back_to_back_us is the mean of `steps` prefill calls launched back to back between one event
+pair: longer than the per-call median, because the sustained MFMA load with no store between
+two calls runs at a lower engine clock.  The store is also reported back to back
+(store_batched_*).
 Prefill legs are timed in steady state: after the warm-up calls, 10 calls are timed at once
 (cold_prefill_call), the matrix cores are then kept busy for settle_s = 1.5 seconds (the
 first sustained MFMA work of a process runs slower while the engine clock settles: the
@@ -41,7 +48,11 @@ then are the `steps` reported calls timed.
 peaks = the spec peaks beside CUs x max engine clock x 4096 flop/clock (bf16 MFMA) from the
 device properties.
 qk_norm_rope_store = the fused q/k RMSNorm + rotary + KV store over C3's 16384 prompt
-tokens and C2's 64 decode tokens: algorithmic bytes / mean event time vs 8 TB/s.
+tokens and C2's 64 decode tokens: algorithmic bytes / mean event time vs 8 TB/s.  The
+short HBM legs (this one, add_rms_norm and the prefill legs' store) also report batched_*:
+`steps` back-to-back calls between one event pair, per call.  An event pair around each
+call adds a few microseconds of launch and event overhead, a large share of a 20-us
+kernel; the batched figure keeps only the gaps between consecutive kernels.
 add_rms_norm = the fused residual add + RMSNorm over the same token counts' 4096-wide
 hidden rows (the norm in front of each block's projections), same figures.
 block_manager = host wall time of the C++ block manager (through the binding): admitting
@@ -73,6 +84,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import sys
@@ -287,14 +299,26 @@ def bench_decode(dev, steps, warmup, graph=True):
     dec_bytes = acc.decode_bytes(case.context_lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
                                  sh.block_size, sh.elem_bytes)
     st_bytes = acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
+    # The decode call alone, `steps` calls back to back over the rotated pool copies between
+    # one event pair: its average launch duration without the per-call event pairs, which
+    # add a few microseconds each.
+    rot = itertools.count()
+
+    def decode_only():
+        kc, vc = sets[next(rot) % 3]
+        nkv.nkv_paged_attn_decode(case.q, kc, vc, lens_d, table_d, sh.scale, out=out, workspace=ws)
+
+    dec_batched_ms = batched_us(decode_only, steps) * 1e-3
     log(f"[decode C2] step {ms_step*1e3:.1f} us (store {store_ms*1e3:.1f} us, decode "
-        f"{dec_ms*1e3:.1f} us) -> decode {dec_bytes/dec_ms/1e6:.0f} GB/s, wall {wall:.3f}s")
+        f"{dec_ms*1e3:.1f} us) -> decode {dec_bytes/dec_ms/1e6:.0f} GB/s, wall {wall:.3f}s; "
+        f"decode calls back to back {dec_batched_ms*1e3:.1f} us -> {dec_bytes/dec_batched_ms/1e6:.0f} GB/s")
 
     # The same steps replayed from HIP graphs, captured after a warm-up call on a side
     # stream.  The calls allocate, memset and synchronise nothing.
     if not graph:
         return dict(case=case, ms_step=ms_step, store_ms=store_ms, dec_ms=dec_ms, dec_bytes=dec_bytes,
-                    st_bytes=st_bytes, workspace_bytes=need, dec_stats=dec_stats, store_stats=store_stats)
+                    st_bytes=st_bytes, workspace_bytes=need, dec_stats=dec_stats, store_stats=store_stats,
+                    dec_batched_ms=dec_batched_ms)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -326,7 +350,7 @@ def bench_decode(dev, steps, warmup, graph=True):
     log(f"[decode C2, graph replay] step {graph_ms_step*1e3:.1f} us over {steps} steps")
     return dict(case=case, ms_step=ms_step, store_ms=store_ms, dec_ms=dec_ms, dec_bytes=dec_bytes,
                 st_bytes=st_bytes, workspace_bytes=need, dec_stats=dec_stats, store_stats=store_stats,
-                graph_ms_step=graph_ms_step, engine_clock=clk.summary())
+                dec_batched_ms=dec_batched_ms, graph_ms_step=graph_ms_step, engine_clock=clk.summary())
 
 
 def prefill_inputs(dev, which):
@@ -348,6 +372,20 @@ def prefill_inputs(dev, which):
     cu_q, cu_k = i32(case.cu_seqlens_q, dev), i32(case.cu_seqlens_k, dev)
     table, slots = i32(case.block_table, dev), i32(case.slot_mapping, dev)
     return case, kc, vc, cu_q, cu_k, table, slots, torch.empty_like(case.q)
+
+
+def batched_us(call, n):
+    """Mean time per call of n back-to-back calls between one event pair: the launch and
+    event overheads that a per-call event pair adds to a kernel of tens of microseconds are
+    left out; the gaps between consecutive kernels stay in."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
 
 
 def bench_prefill(dev, which, steps, warmup, settle_s=1.5):
@@ -392,6 +430,13 @@ def bench_prefill(dev, which, steps, warmup, settle_s=1.5):
         evs = timed(steps)
     st_stats = stats_us([e[0].elapsed_time(e[1]) for e in evs])
     pf_stats = stats_us([e[1].elapsed_time(e[2]) for e in evs])
+    st_batched = batched_us(lambda: nkv.nkv_store_kvcache(case.k, case.v, kc, vc, slots), steps)
+    # `steps` prefill calls back to back as well: reported beside the per-call median, which
+    # stays the leg's time (back to back, the sustained MFMA load runs at a lower engine
+    # clock than the steps with a store between two calls, and takes longer)
+    pf_batched = batched_us(lambda: nkv.nkv_paged_attn_prefill(case.q, kc, vc, cu_q, cu_k, table,
+                                                                 case.max_seqlen_q, case.max_seqlen_k,
+                                                                 sh.scale, out=out), steps)
     # The median call: a rare stall of tens of milliseconds inside one timed interval (seen
     # on some boxes, in either leg and in the store before it) would otherwise dominate the
     # mean of 50 sub-ms calls; the means stay in prefill_call and store_call.
@@ -400,13 +445,18 @@ def bench_prefill(dev, which, steps, warmup, settle_s=1.5):
     flops = acc.prefill_flops(case.cu_seqlens_q, case.cu_seqlens_k, sh.num_q_heads, sh.head_dim)
     st_bytes = acc.store_bytes(case.slot_mapping, sh.num_kv_heads, sh.head_dim, sh.elem_bytes)
     tflops = flops / pf_ms / 1e9
-    log(f"[prefill {which}] store {store_ms*1e3:.1f} us ({st_bytes/store_ms/1e6:.0f} GB/s), "
-        f"prefill {pf_ms*1e3:.1f} us -> {tflops:.1f} TFLOP/s")
+    log(f"[prefill {which}] store {store_ms*1e3:.1f} us ({st_bytes/store_ms/1e6:.0f} GB/s; back to back "
+        f"{st_batched:.1f} us -> {st_bytes/st_batched/1e3:.0f} GB/s), prefill {pf_ms*1e3:.1f} us "
+        f"({pf_batched:.1f} us back to back) -> {tflops:.1f} TFLOP/s")
     return {"workload": which, "prefill_us": round(pf_ms * 1e3, 2),
             "tflops": round(tflops, 2), "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "back_to_back_us": round(pf_batched, 2),
             "flop": flops, "prefill_call": pf_stats, "cold_prefill_call": cold,
             "settle_s": settle_s, "store_us": round(store_ms * 1e3, 2), "store_call": st_stats,
             "store_gbs": round(st_bytes / store_ms / 1e6, 1),
+            "store_batched_us": round(st_batched, 2),
+            "store_batched_gbs": round(st_bytes / st_batched / 1e3, 1),
+            "store_batched_frac_of_hbm_peak": round(st_bytes / st_batched / 1e3 / HBM_PEAK_GBS, 4),
             "engine_clock": clk.summary(),
             "roofline": prefill_roofline(which, tflops, flops, pf_ms * 1e3,
                                          prefill_counter_record(kernel_source_sha(PREFILL_SOURCES)))}
@@ -456,11 +506,13 @@ def bench_varlen_prefill(dev, steps, warmup, settle_s=1.5):
             call()
         torch.cuda.synchronize()
     st = timed(steps)
+    bt = batched_us(call, steps)
     flops = acc.prefill_flops(cu, cu, hq, d)
     tflops = flops / (st["median_us"] * 1e-6) / 1e12
-    log(f"[varlen prefill C3] {st['median_us']:.1f} us -> {tflops:.1f} TFLOP/s")
+    log(f"[varlen prefill C3] {st['median_us']:.1f} us ({bt:.1f} us back to back) -> {tflops:.1f} TFLOP/s")
     return {"workload": "C3 prompts, contiguous K/V views of a packed qkv", "prefill_us": st["median_us"],
             "tflops": round(tflops, 2), "frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "back_to_back_us": round(bt, 2),
             "flop": flops, "prefill_call": st, "cold_prefill_call": cold, "settle_s": settle_s}
 
 
@@ -563,12 +615,16 @@ def bench_rope_store(dev, which, steps, warmup):
         b.record()
     torch.cuda.synchronize()
     st = stats_us([a.elapsed_time(b) for a, b in evs])
+    bt = batched_us(call, steps)
     nbytes = acc.qk_norm_rope_store_bytes(case.slot_mapping, sh.num_q_heads, sh.num_kv_heads,
                                           sh.head_dim, sh.elem_bytes)
     gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
-    log(f"[qk-norm+rope+store {which}] {t} tokens: {st['mean_us']:.1f} us -> {gbs:.0f} GB/s")
+    bgbs = nbytes / (bt * 1e-6) / 1e9
+    log(f"[qk-norm+rope+store {which}] {t} tokens: {st['mean_us']:.1f} us -> {gbs:.0f} GB/s "
+        f"(batched {bt:.1f} us -> {bgbs:.0f} GB/s)")
     return {"workload": f"{which} tokens ({t})", "call": st, "bytes": nbytes, "gbs": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "batched_us": round(bt, 2),
+            "batched_gbs": round(bgbs, 1), "batched_frac_of_hbm_peak": round(bgbs / HBM_PEAK_GBS, 4)}
 
 
 def bench_add_rms_norm(dev, which, steps, warmup):
@@ -599,11 +655,16 @@ def bench_add_rms_norm(dev, which, steps, warmup):
         b.record()
     torch.cuda.synchronize()
     st = stats_us([a.elapsed_time(b) for a, b in evs])
+    bt = batched_us(call, steps)
     nbytes = acc.add_rms_norm_bytes(t, h, 2)
     gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
-    log(f"[add+rmsnorm {which}] {t} x {h}: {st['mean_us']:.1f} us -> {gbs:.0f} GB/s")
+    bgbs = nbytes / (bt * 1e-6) / 1e9
+    log(f"[add+rmsnorm {which}] {t} x {h}: {st['mean_us']:.1f} us -> {gbs:.0f} GB/s "
+        f"(batched {bt:.1f} us -> {bgbs:.0f} GB/s)")
     return {"workload": f"{which} tokens ({t}) x hidden {h}", "call": st, "bytes": nbytes,
-            "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "batched_us": round(bt, 2), "batched_gbs": round(bgbs, 1),
+            "batched_frac_of_hbm_peak": round(bgbs / HBM_PEAK_GBS, 4)}
 
 
 def blas_threads():
@@ -1089,7 +1150,7 @@ def main():
 
     step_bytes = d["dec_bytes"] + d["st_bytes"]
     value = step_bytes / d["graph_ms_step"] / 1e6
-    achieved = d["dec_bytes"] / d["dec_ms"] / 1e6
+    achieved = d["dec_bytes"] / d["dec_batched_ms"] / 1e6
     sha = kernel_source_sha(DECODE_SOURCES)
     case = d["case"]
     line = {
@@ -1125,7 +1186,10 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_counters(sha),
             "algorithmic_bytes_per_launch": int(d["dec_bytes"]),
-            "avg_launch_us": round(d["dec_ms"] * 1e3, 2),
+            "avg_launch_us": round(d["dec_batched_ms"] * 1e3, 2),
+            "timing": f"{args.steps} decode calls back to back over the 3 rotated pool copies "
+                      "between one event pair on the launch stream, per call",
+            "per_call_event_us": round(d["dec_ms"] * 1e3, 2),
             "kernel_source_sha": sha,
         },
         "decode_call": d["dec_stats"],
