@@ -122,6 +122,19 @@ __device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, v
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_addr(lds_base)) : "memory");
 }
+// The same two copies with the LDS destination given as an LDS byte address (uniform).
+// No immediate offset is used: the instruction's offset field moves the LDS destination
+// as well as the global address.
+__device__ __forceinline__ void load_lds16_s_at(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void load_lds16_at(const void* gptr, uint32_t lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(gptr), "s"(lds) : "memory");
+}
 // The same with the nontemporal hint, for data read once and not again soon (a decode
 // step's K/V stream): it leaves less of the caches to lines that will not be reused.
 __device__ __forceinline__ void load_lds16_s_nt(const void* sbase, uint32_t voff, void* lds_base) {

@@ -8,9 +8,11 @@
 // Lk - Lq + i and sees keys j <= Lk - Lq + i.
 //
 // bf16 path (dense contraction -> MFMA, v_mfma_f32_16x16x32_bf16):
-//   grid (seq * kv_head, q-tile), q-tiles dispatched longest-first.  A workgroup of 8
-//   waves (two per SIMD) holds the G query heads of one KV head; each wave owns 32
-//   queries of one head, two 16-query MFMA column blocks.  K/V tiles of 128 keys are
+//   grid (seq * kv_head, pair of consecutive q-tiles), longest pairs dispatched first.  A
+//   workgroup of 8 waves (two per SIMD) holds the G query heads of one KV head; each wave
+//   owns 32 queries of one head, two 16-query MFMA column blocks.  The second q-tile of a
+//   pair starts on the first one's last K/V tile, still in LDS, and its q is copied into
+//   LDS during that tile, so it needs no prologue of its own.  K/V tiles of 128 keys are
 //   gathered through the block table into a double-buffered LDS stage shared by all
 //   waves: K and V rows are copied HBM -> LDS directly, by waves 0-3 only (global_load_lds,
 //   chunk c of row t at c ^ kv_swz(t), free of bank conflicts for both kinds of read).  K fragments are 16-byte LDS reads; V^T
@@ -46,6 +48,9 @@ namespace nkv {
 #ifndef NKV_PREFILL_PRIO
 #define NKV_PREFILL_PRIO 0
 #endif
+#ifndef NKV_PREFILL_PAIR
+#define NKV_PREFILL_PAIR 1
+#endif
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;   // one transposing LDS read
 
@@ -54,6 +59,7 @@ constexpr int kStages = 2;              // K/V tiles in LDS (one computed, one l
 constexpr float kLazyBound = 256.0f;    // largest weight kept before rescaling (2^8 headroom)
 constexpr int kMaxIds = kBK / 16;       // block ids per tile (block_size >= 16)
 constexpr int kLog2BK = kBK == 128 ? 7 : 6;
+constexpr bool kPairQTiles = NKV_PREFILL_PAIR;   // two consecutive q-tiles per workgroup
 static_assert(kBK == 64 || kBK == 128, "64- or 128-key tiles");
 
 // Swizzle of the 16-byte chunks of a K/V tile row in LDS: logical chunk c of row t sits at
@@ -91,10 +97,12 @@ struct PfGeom {
   static constexpr int STAGE = 2 * K_BYTES;     // K rows, then V rows, same layout
   static constexpr int CW = NW / 2;             // waves that issue the K/V copies (the first half)
   static constexpr int K_DMA = K_BYTES / 1024 / CW;   // copy instructions per copying wave per tile (K or V)
-  static constexpr int OROW = D * 2 + 16;             // output staging row stride (bytes)
   static_assert(G >= 1 && G <= NW && NW % G == 0, "GQA group must divide the waves");
   static_assert(K_DMA >= 1 && K_BYTES % (1024 * CW) == 0, "K tile must split over the copying waves");
-  static constexpr int SMEM = kStages * STAGE > NW * WQ * OROW ? kStages * STAGE : NW * WQ * OROW;
+  // a q-tile's q (NW * WQ rows of D) fills one stage exactly: the next q-tile's q lands in
+  // the stage the last tile leaves free, and each wave stages its output rows in its share
+  static_assert(NW * WQ == 2 * kBK, "a q-tile's q must fill one stage");
+  static constexpr int SMEM = kStages * STAGE;
 };
 
 template <int D, int G, int NW>
@@ -109,18 +117,27 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   using Geo = PfGeom<D, G, NW>;
   constexpr int KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, WQ = Geo::WQ;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Geo::SMEM];
-  __shared__ int32_t s_ids[3][kMaxIds];               // block ids of tiles t, t+1, t+2
+  __shared__ int32_t s_ids[3][kMaxIds];               // block ids of positions p, p+1, p+2
 
   const int pair = blockIdx.x;
   const int b = pair / num_kv_heads;
   const int g = pair - b * num_kv_heads;
-  const int qt = gridDim.y - 1 - blockIdx.y;          // longest tiles first
+  const int qt = (gridDim.y - 1 - blockIdx.y) * (kPairQTiles ? 2 : 1);   // longest tiles first
   const int qstart = cu_q[b];
   const int lq = cu_q[b + 1] - qstart;
   const int lk = cu_k[b + 1] - cu_k[b];
-  const int q0 = qt * Geo::BQ;
+  int q0 = qt * Geo::BQ;
   if (q0 >= lq) return;
   const int diag = lk - lq;                           // query i sees keys <= diag + i
+  // A workgroup computes q-tile qt and then, if it exists, q-tile qt + 1 ("b").  Tile
+  // buffer positions p = 0 .. nsteps-1 hold K/V tile p mod nb: q-tile qt takes positions
+  // 0 .. na-1 (tiles 0 .. na-1), and b starts on position na-1 again, the last tile of qt,
+  // still in LDS (b's keys include all of qt's), then takes na .. nsteps-1 (tiles na ..
+  // nb-1, then 0 .. na-2).  b's q is copied into the free stage during qt's last tile.
+  const bool has_b = kPairQTiles && q0 + Geo::BQ < lq;
+  const int na = (diag + min(q0 + Geo::BQ, lq) + kBK - 1) / kBK;
+  const int nb = has_b ? (diag + min(q0 + 2 * Geo::BQ, lq) + kBK - 1) / kBK : na;
+  const int nsteps = has_b ? na + nb - 1 : na;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,10 +147,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   const int hq = G * num_kv_heads;
   const int col = lane & 15;                          // MFMA column: query of a 16-block
   const int quad = lane >> 4;                         // MFMA lane quarter
-  const int wq0 = q0 + (wave / G) * WQ;               // this wave's first query
-  const int kend = diag + min(q0 + Geo::BQ, lq);      // keys the workgroup needs
-  const int ntiles = (kend + kBK - 1) / kBK;
-  const int wkend = wq0 < lq ? diag + min(wq0 + WQ, lq) : 0;   // keys this wave needs
+  int wq0 = q0 + (wave / G) * WQ;                     // this wave's first query
+  int wkend = wq0 < lq ? diag + min(wq0 + WQ, lq) : 0;   // keys this wave needs
   // paged: keys through the block table; otherwise rows kv0.. of contiguous k/v
   const bool paged = block_table != nullptr;
   const int64_t kv0 = paged ? 0 : cu_k[b];
@@ -160,14 +175,16 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   }
 
   // ---- copies: block ids two tiles ahead (LDS), K and V rows by DMA ----
-  auto issue_ids = [&](int t) {                       // wave 0: ids of tile t -> s_ids[t % 3]
+  // Position p holds tile p mod nb in stage p % kStages, its block ids in s_ids[p % 3].
+  auto tile_at = [&](int p) __attribute__((always_inline)) { return p < nb ? p : p - nb; };
+  auto issue_ids = [&](int p) __attribute__((always_inline)) {                       // wave 0: ids of position p -> s_ids[p % 3]
     if (paged && wave == 0 && lane < ids_per_tile) {
-      const int blk = min(((t * kBK) >> log2_bs) + lane, last_blk);
-      load_lds4(trow + blk, &s_ids[t % 3][0]);
+      const int blk = min(((tile_at(p) * kBK) >> log2_bs) + lane, last_blk);
+      load_lds4(trow + blk, &s_ids[p % 3][0]);
     }
   };
-  auto row_off = [&](int t, int key) -> int64_t {     // element offset of (key, head g)
-    const int64_t phys = s_ids[t % 3][((key - t * kBK) >> log2_bs) & (kMaxIds - 1)];
+  auto row_off = [&](int p, int key) __attribute__((always_inline)) -> int64_t {     // element offset of (key, head g)
+    const int64_t phys = s_ids[p % 3][((key - tile_at(p) * kBK) >> log2_bs) & (kMaxIds - 1)];
     return ((phys << log2_bs) + (key & bs_mask)) * row_elems;
   };
   // The K/V copies of a tile are issued by waves 0..NW/2-1 only.  A wave waits at each copy
@@ -177,65 +194,123 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // meanwhile (C3 loop 3.80 -> 3.49 us per tile).
   const bool copier = wave < Geo::CW;
   const int cwave = wave % Geo::CW;
-  int k_row[Geo::K_DMA], k_elem[Geo::K_DMA];
-#pragma unroll
-  for (int j = 0; j < Geo::K_DMA; ++j) {
-    const int s = (cwave * Geo::K_DMA + j) * 64 + lane;  // LDS slot this lane fills
-    k_row[j] = s / CPR;
-    k_elem[j] = ((s % CPR) ^ kv_swz<CPR>(k_row[j])) * 8;
-  }
+  // Copy j of a copying wave fills LDS slots (cwave * K_DMA + j) * 64 + lane: the lane's
+  // row is r0 + j * RPI and its element the swizzled chunk of that row, which repeats
+  // every NE copies (the swizzle sees the row mod 16, or mod 8 for 64-dim rows).
+  constexpr int RPI = 64 / CPR;                        // rows per copy instruction
+  constexpr int NE = CPR == 16 ? 16 / RPI : 1;         // distinct chunk swizzles over j
+  static_assert(Geo::K_DMA % NE == 0, "copies per wave must cover whole swizzle periods");
+  const int r0 = cwave * Geo::K_DMA * RPI + lane / CPR;
+  auto k_row = [&](int j) __attribute__((always_inline)) { return r0 + j * RPI; };
+  auto k_elem = [&](int j) __attribute__((always_inline)) { return ((lane % CPR) ^ kv_swz<CPR>(r0 + j * RPI)) * 8; };
   // With block_size >= kBK a tile lies inside one physical block: its base is uniform
   // (one LDS read, scalar math) and each lane adds only row * stride.  Contiguous K/V is
   // one such "block".
   const bool tile_in_block = !paged || log2_bs >= kLog2BK;
-  auto tile_base = [&](int t, const uint16_t* base, int64_t stride) {
+  auto tile_base = [&](int p, const uint16_t* base, int64_t stride) __attribute__((always_inline)) {
+    const int t = tile_at(p);
     if (!paged) return base + (kv0 + int64_t(t) * kBK) * stride;
-    const int phys = __builtin_amdgcn_readfirstlane(s_ids[t % 3][0]);
+    const int phys = __builtin_amdgcn_readfirstlane(s_ids[p % 3][0]);
     return base + ((int64_t(phys) << log2_bs) + ((t * kBK) & bs_mask)) * stride;
   };
-  // K and V rows of tile t go HBM -> LDS directly, each into its half of stage t % 2
-  // (region 0: K, K_BYTES: V) in the same swizzled row layout.  Inside a tile the rows
-  // are at most kBK - 1 strides from its base; with strides below 2^23 elements the byte
-  // offsets fit 32 bits, so a copy is a wave-uniform base plus a per-lane offset fixed
-  // for the whole kernel (full tiles) instead of 64-bit lane arithmetic (C3 310 -> 304 us).
+  // K and V rows of the tile at position p go HBM -> LDS directly, each into its half of
+  // stage p % 2 (region 0: K, K_BYTES: V) in the same swizzled row layout.  Inside a tile
+  // the rows are at most kBK - 1 strides from its base; with strides below 2^23 elements
+  // the byte offsets fit 32 bits, so a copy of a full tile is a wave-uniform base (the
+  // tile's, plus j * RPI rows) and a per-lane offset fixed for the whole kernel (one of
+  // NE) instead of 64-bit lane arithmetic (C3 310 -> 304 us).
   const bool off32 = k_stride < (int64_t(1) << 23) && v_stride < (int64_t(1) << 23);
-  uint32_t koff[Geo::K_DMA], voff[Geo::K_DMA];
+  uint32_t koff[NE], voff[NE];
 #pragma unroll
-  for (int j = 0; j < Geo::K_DMA; ++j) {
-    koff[j] = uint32_t((k_row[j] * k_stride + k_elem[j]) * 2);
-    voff[j] = uint32_t((k_row[j] * v_stride + k_elem[j]) * 2);
+  for (int e = 0; e < NE; ++e) {
+    koff[e] = uint32_t((r0 * k_stride + k_elem(e)) * 2);
+    voff[e] = uint32_t((r0 * v_stride + k_elem(e)) * 2);
   }
-  auto issue_rows_at = [&](int t, const uint16_t* tb, int64_t stride, int region) {   // tile inside one block
-    uint8_t* sk = smem + (t % kStages) * Geo::STAGE + region;
-    const int rmax = lk - 1 - t * kBK;               // rows past the keys repeat the last
+  auto issue_rows_at = [&](int p, const uint16_t* tb, int64_t stride, int region) __attribute__((always_inline)) {   // tile inside one block
+    uint8_t* sk = smem + (p % kStages) * Geo::STAGE + region;
+    const int rmax = lk - 1 - tile_at(p) * kBK;      // rows past the keys repeat the last
     if (off32) {
       if (rmax >= kBK - 1) {
 #pragma unroll
-        for (int j = 0; j < Geo::K_DMA; ++j)
-          load_lds16_s(tb, region == 0 ? koff[j] : voff[j], sk + (cwave * Geo::K_DMA + j) * 1024);
+        for (int j = 0; j < Geo::K_DMA; ++j) {
+          load_lds16_s(tb, region == 0 ? koff[j % NE] : voff[j % NE], sk + (cwave * Geo::K_DMA + j) * 1024);
+          tb += RPI * stride;
+          asm volatile("" : "+s"(tb));     // advanced copy by copy, not precomputed for all j
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < Geo::K_DMA; ++j)
-          load_lds16_s(tb, uint32_t((min(k_row[j], rmax) * stride + k_elem[j]) * 2),
+          load_lds16_s(tb, uint32_t((min(k_row(j), rmax) * stride + k_elem(j)) * 2),
                        sk + (cwave * Geo::K_DMA + j) * 1024);
       }
       return;
     }
 #pragma unroll
     for (int j = 0; j < Geo::K_DMA; ++j)
-      load_lds16(tb + min(k_row[j], rmax) * stride + k_elem[j], sk + (cwave * Geo::K_DMA + j) * 1024);
+      load_lds16(tb + min(k_row(j), rmax) * stride + k_elem(j), sk + (cwave * Geo::K_DMA + j) * 1024);
   };
-  auto issue_rows = [&](int t, const uint16_t* base, int64_t stride, int region) {
+  auto issue_rows = [&](int p, const uint16_t* base, int64_t stride, int region) __attribute__((always_inline)) {
     if (!copier) return;
     if (tile_in_block) {
-      issue_rows_at(t, tile_base(t, base, stride), stride, region);
+      issue_rows_at(p, tile_base(p, base, stride), stride, region);
     } else {
-      uint8_t* sk = smem + (t % kStages) * Geo::STAGE + region;
+      uint8_t* sk = smem + (p % kStages) * Geo::STAGE + region;
+      const int t = tile_at(p);
       const int rmax = lk - 1 - t * kBK;
 #pragma unroll
       for (int j = 0; j < Geo::K_DMA; ++j) {
-        const int key = t * kBK + min(k_row[j], rmax);
-        load_lds16(base + row_off(t, key) + k_elem[j], sk + (cwave * Geo::K_DMA + j) * 1024);
+        const int key = t * kBK + min(k_row(j), rmax);
+        load_lds16(base + row_off(p, key) + k_elem(j), sk + (cwave * Geo::K_DMA + j) * 1024);
+      }
+    }
+  };
+  // q of q-tile b into the stage at position p, in MFMA fragment order: fragment
+  // f = (wave w, query block j, k-step ks) is 1 KB at f * 1024, lane L's 16 bytes being
+  // dims 32 ks + 8 (L >> 4) .. of query 16 j + (L & 15) of wave w, so a wave later reads
+  // each of its fragments with one conflict-free 16-byte LDS read per lane.  Copying wave
+  // c copies the fragments of waves 2c and 2c + 1 from one uniform base (the q-tile's
+  // first row) and a per-lane byte offset (query block and k-step; the instruction's own
+  // offset field would move the LDS destination too).  A partial q-tile repeats its last
+  // query (never written out).  The
+  // offsets stay below 2^31 when q_row * BQ < 2^30; otherwise each lane takes a 64-bit
+  // address.
+  static_assert(2 * Geo::CW == Geo::NW, "each copying wave copies the q of two waves");
+  auto issue_q = [&](int p) __attribute__((always_inline)) {
+    // this wave's fragments are one contiguous run of 4 * KS KB; the LDS address advances
+    // copy by copy (opaque, so the compiler keeps one register, not one per copy)
+    uint32_t la = lds_addr(smem + (p % kStages) * Geo::STAGE + cwave * (4 * KS * 1024));
+    const int qb0 = q0 + Geo::BQ;
+    const uint16_t* qb = q + int64_t(qstart + qb0) * q_row + int64_t(g) * G * D;
+    const bool off32 = q_row * Geo::BQ < (int64_t(1) << 30);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));                    // as in the epilogue: no hoisted lane math
+    const int col = ln & 15, quad = ln >> 4;
+    auto next = [&]() __attribute__((always_inline)) {
+      la += 1024;
+      asm volatile("" : "+s"(la));
+    };
+#pragma unroll
+    for (int wi = 0; wi < 2; ++wi) {
+      const int w = 2 * cwave + wi;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int qr = min((w / G) * WQ + 16 * j + col, lq - 1 - qb0);   // row in the q-tile
+        const int eo = (w % G) * D + 8 * quad;                            // element in the row
+        if (off32) {
+          const uint32_t voff = uint32_t((qr * q_row + eo) * 2);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            load_lds16_s_at(qb, voff + 64 * ks, la);
+            next();
+          }
+        } else {
+          const uint16_t* lp = qb + int64_t(qr) * q_row + eo;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            load_lds16_at(lp + 32 * ks, la);
+            next();
+          }
+        }
       }
     }
   };
@@ -254,7 +329,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // A lane's fragment rows are a multiple of 16 plus col (K) or v_row (V^T), so their
   // swizzle is fixed per lane.
   const int swz_k = kv_swz<CPR>(col);
-  auto read_k = [&](const uint8_t* st, int kb, bf16x8_t (&kf)[2][KS]) {
+  auto read_k = [&](const uint8_t* st, int kb, bf16x8_t (&kf)[2][KS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int t = kb * 32 + 16 * i + col;
@@ -269,7 +344,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // 4*quad + r and 16 + 4*quad + r that the lane's P^T operand holds, in that order.
   const int v_row = 4 * quad + (col >> 2), v_dim = 4 * (col & 3);
   const int swz_v = kv_swz<CPR>(v_row);
-  auto read_v = [&](const uint8_t* st, int kb, bf16x8_t (&vf)[DT]) {
+  auto read_v = [&](const uint8_t* st, int kb, bf16x8_t (&vf)[DT]) __attribute__((always_inline)) {
     const uint8_t* sv = st + Geo::K_BYTES;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -283,14 +358,14 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       vf[dt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
-  auto qk = [&](const bf16x8_t (&kf)[KS], int j, f32x4_t& s) {
+  auto qk = [&](const bf16x8_t (&kf)[KS], int j, f32x4_t& s) __attribute__((always_inline)) {
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[j][0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[j][ks], s, 0, 0, 0);
   };
   // Weights of one 16x16 block of S^T against max mq, as two bf16 pairs, and their sum.
-  auto weights = [&](const f32x4_t& s, float cs, float mq, uint32_t& w0, uint32_t& w1) {
+  auto weights = [&](const f32x4_t& s, float cs, float mq, uint32_t& w0, uint32_t& w1) __attribute__((always_inline)) {
     w0 = pack_bf16x2(fast_exp2(fmaf(s[0], cs, -mq)), fast_exp2(fmaf(s[1], cs, -mq)));
     w1 = pack_bf16x2(fast_exp2(fmaf(s[2], cs, -mq)), fast_exp2(fmaf(s[3], cs, -mq)));
     return dot2_bf16(w1, ones, dot2_bf16(w0, ones, 0.f));
@@ -305,10 +380,12 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // before the first half) does the wave raise m to the max of the half's scores of
   // that block (over the four lanes of each query), rescale O and l, and take the
   // weights again.  Every weight is at most that sum, so no weight kept exceeds
-  // kLazyBound, the same headroom as testing the max itself.  Key 0, visible to every
-  // query, lies in the first half, so m is finite from then on.  Block 0's weights are
-  // computed while block 1's QK MFMAs run.
-  auto softmax_pv = [&](f32x4_t (&s)[2][2], int k0h, const bf16x8_t (&vf)[DT]) {
+  // kLazyBound, the same headroom as testing the max itself.  The first half a q-tile
+  // computes holds a key every one of its queries sees (key 0; for the second q-tile of a
+  // pair, the first key of the first one's last tile, which lies before its first
+  // query's diagonal), so m is finite from then on.  Block 0's weights are computed while
+  // block 1's QK MFMAs run.
+  auto softmax_pv = [&](f32x4_t (&s)[2][2], int k0h, const bf16x8_t (&vf)[DT]) __attribute__((always_inline)) {
     const bool masked = (k0h + 31 > diag + wq0) || (k0h + 32 > lk);
     const float cs = masked ? 1.0f : scale_log2e;
     if (masked) {
@@ -357,7 +434,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   };
   // One 32-key half: QK of key block 0 for both query blocks, then of key block 1 (the
   // softmax of block 0 can run beside those MFMAs), then softmax and P.V.
-  auto half = [&](const uint8_t* st, int kb, int k0h) {
+  auto half = [&](const uint8_t* st, int kb, int k0h) __attribute__((always_inline)) {
     bf16x8_t kf[2][KS], vf[DT];
     f32x4_t s[2][2];
     read_k(st, kb, kf);
@@ -372,7 +449,47 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     softmax_pv(s, k0h, vf);
   };
 
-  // ---- prologue: tile 0 into stage 0, ids of tiles 1..2 ----
+  // ---- epilogue: O^T / l -> bf16 rows staged in LDS, then contiguous row writes ----
+  // The wave's 32 output rows go to `ost` (its own 64 * D bytes), 16-byte chunk c of row r
+  // at c ^ (r mod CPR), and are read back a row per CPR lanes.  A wave reads back only the
+  // rows it wrote, and LDS keeps one wave's accesses in order, so no barrier sits between.
+  auto epilogue = [&](uint8_t* ost) __attribute__((always_inline)) {
+    // lane-derived addresses are made here, not hoisted out of the tile loop (where this
+    // also runs, between the two q-tiles) to sit in registers through every tile
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int col = ln & 15, quad = ln >> 4;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // the four lanes of a query hold different keys
+      const float inv = 1.0f / xor32_sum(xor16_sum(lsum[j]));
+      if (wq0 + 16 * j < lq) {
+        const int r = 16 * j + col;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int c = 2 * dt + (quad >> 1);
+          const u32x2_t w = {pack_bf16x2(o[j][dt][0] * inv, o[j][dt][1] * inv),
+                             pack_bf16x2(o[j][dt][2] * inv, o[j][dt][3] * inv)};
+          *reinterpret_cast<u32x2_t*>(ost + r * (D * 2) + (c ^ (r & (CPR - 1))) * 16 + (quad & 1) * 8) = w;
+        }
+      }
+    }
+    if (wq0 < lq) {
+      constexpr int RPI = 64 / CPR;               // rows per 64-lane pass
+      const int rr = ln / CPR, cc = ln % CPR;
+#pragma unroll 1
+      for (int i = 0; i < WQ / RPI; ++i) {
+        const int row = i * RPI + rr;
+        const int qi = wq0 + row;
+        if (qi < lq) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ost + row * (D * 2) + (cc ^ (row & (CPR - 1))) * 16);
+          *reinterpret_cast<u32x4_t*>(out + (int64_t(qstart + qi) * hq + h) * D + cc * 8) = v;
+        }
+      }
+    }
+  };
+
+  // ---- prologue: tile 0 into stage 0, ids of positions 1..2 ----
   if (tile_in_block) {
     // tile 0's block id comes straight from the table (one scalar load), so its copies
     // go out beside the q loads instead of after a round trip through s_ids
@@ -387,68 +504,73 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       issue_rows_at(0, k0b, k_stride, 0);
       issue_rows_at(0, v0b, v_stride, Geo::K_BYTES);
     }
-    if (ntiles > 1) issue_ids(1);
-    if (ntiles > 2) issue_ids(2);
+    if (nsteps > 1) issue_ids(1);
+    if (nsteps > 2) issue_ids(2);
   } else {
     issue_ids(0);
-    if (ntiles > 1) issue_ids(1);
+    if (nsteps > 1) issue_ids(1);
     wait_vmem_all();
     __syncthreads();
     issue_rows(0, kbase, k_stride, 0);
     issue_rows(0, vbase, v_stride, Geo::K_BYTES);
-    if (ntiles > 2) issue_ids(2);
+    if (nsteps > 2) issue_ids(2);
   }
   wait_vmem_all();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) {                                   // next tile's copies fly during this one
-      issue_rows(t + 1, kbase, k_stride, 0);
-      issue_rows(t + 1, vbase, v_stride, Geo::K_BYTES);
-      if (t + 3 < ntiles) issue_ids(t + 3);
+  // One tile step at position p: the next position's copies (or, on qt's last tile, b's
+  // q) go out first and fly during this tile's math; ids go two positions further ahead.
+  auto step = [&](int p, bool a_last, bool b_first) __attribute__((always_inline)) {
+    if (a_last) {
+      if (has_b && copier) issue_q(p + 1);
+    } else if (p + 1 < nsteps) {
+      issue_rows(p + 1, kbase, k_stride, 0);
+      issue_rows(p + 1, vbase, v_stride, Geo::K_BYTES);
     }
-    const int k0 = t * kBK;
-    const uint8_t* st = smem + (t % kStages) * Geo::STAGE;
+    if (!b_first && p + 3 < nsteps) issue_ids(p + 3);
+    const int k0 = tile_at(p) * kBK;
+    const uint8_t* st = smem + (p % kStages) * Geo::STAGE;
 #pragma unroll
     for (int kb = 0; kb < kBK / 32; ++kb)
       if (k0 + 32 * kb < wkend) half(st, kb, k0 + 32 * kb);
     wait_vmem_all();
     __syncthreads();
+  };
+  int p = 0;
+  bool in_b = false;                                  // computing q-tile b
+  for (;;) {
+    const bool a_last = !in_b && p == na - 1;
+    step(p, a_last, in_b && p == na - 1);
+    if (a_last) {
+      if (!has_b) break;
+      // switch to q-tile b: its q fragments from the stage they landed in, then qt's
+      // output staged in the same wave-owned bytes, then fresh running sums
+      uint8_t* qw = smem + ((p + 1) % kStages) * Geo::STAGE + wave * (2 * KS * 1024);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qf[j][ks] = *reinterpret_cast<const bf16x8_t*>(qw + (j * KS + ks) * 1024 + lane * 16);
+      epilogue(qw);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        m[j] = -INFINITY;
+        lsum[j] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[j][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      q0 += Geo::BQ;
+      wq0 += Geo::BQ;
+      wkend = wq0 < lq ? diag + min(wq0 + WQ, lq) : 0;
+      __syncthreads();                              // staging read back before the stage refills
+      in_b = true;
+      continue;                                     // b starts on qt's last tile
+    }
+    if (++p == nsteps) break;
   }
 
-  // ---- epilogue: O^T / l -> bf16 rows staged in LDS, then contiguous row writes ----
-  uint8_t* ost = smem + wave * WQ * Geo::OROW;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    // the four lanes of a query hold different keys
-    const float inv = 1.0f / xor32_sum(xor16_sum(lsum[j]));
-    if (wq0 + 16 * j < lq) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d0 = dt * 16 + 4 * quad;
-        const u32x2_t w = {pack_bf16x2(o[j][dt][0] * inv, o[j][dt][1] * inv),
-                           pack_bf16x2(o[j][dt][2] * inv, o[j][dt][3] * inv)};
-        *reinterpret_cast<u32x2_t*>(ost + (16 * j + col) * Geo::OROW + d0 * 2) = w;
-      }
-    }
-  }
-  // No barrier: a wave reads back only the rows it wrote (LDS keeps one wave's accesses
-  // in order), and the barrier that closed the last tile already has every wave done
-  // with the K/V stages that the staging rows overlap (C3 283 vs 286 us).
-  if (wq0 < lq) {
-    constexpr int RPI = 64 / CPR;                 // rows per 64-lane pass
-    const int rr = lane / CPR, cc = lane % CPR;
-#pragma unroll
-    for (int i = 0; i < WQ / RPI; ++i) {
-      const int row = i * RPI + rr;
-      const int qi = wq0 + row;
-      if (qi < lq) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ost + row * Geo::OROW + cc * 16);
-        *reinterpret_cast<u32x4_t*>(out + (int64_t(qstart + qi) * hq + h) * D + cc * 8) = v;
-      }
-    }
-  }
+  // the barrier that closed the last tile has every wave done with the stages
+  epilogue(smem + wave * (2 * KS * 1024));
 }
 
 // ---- fp32 VALU path --------------------------------------------------------------------
@@ -515,7 +637,8 @@ static hipError_t launch_bf16(const PrefillArgs& a, hipStream_t st) {
   using Geo = PfGeom<D, G, NW>;
   const PagedArgs& p = a.p;
   const int qtiles = (a.max_seqlen_q + Geo::BQ - 1) / Geo::BQ;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW>), dim3(p.num_seqs * p.num_kv_heads, qtiles),
+  const int groups = kPairQTiles ? (qtiles + 1) / 2 : qtiles;   // workgroups per (sequence, KV head)
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW>), dim3(p.num_seqs * p.num_kv_heads, groups),
                      dim3(Geo::NT), 0, st, static_cast<const uint16_t*>(a.q), a.q_row_elems,
                      static_cast<const uint16_t*>(p.k_cache), static_cast<const uint16_t*>(p.v_cache),
                      a.k_row_elems, a.v_row_elems, a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,
