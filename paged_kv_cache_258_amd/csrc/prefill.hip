@@ -267,18 +267,17 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // q of q-tile b into the stage at position p, in MFMA fragment order: fragment
   // f = (wave w, query block j, k-step ks) is 1 KB at f * 1024, lane L's 16 bytes being
   // dims 32 ks + 8 (L >> 4) .. of query 16 j + (L & 15) of wave w, so a wave later reads
-  // each of its fragments with one conflict-free 16-byte LDS read per lane.  Copying wave
-  // c copies the fragments of waves 2c and 2c + 1 from one uniform base (the q-tile's
-  // first row) and a per-lane byte offset (query block and k-step; the instruction's own
-  // offset field would move the LDS destination too).  A partial q-tile repeats its last
-  // query (never written out).  The
-  // offsets stay below 2^31 when q_row * BQ < 2^30; otherwise each lane takes a 64-bit
-  // address.
-  static_assert(2 * Geo::CW == Geo::NW, "each copying wave copies the q of two waves");
+  // each of its fragments with one conflict-free 16-byte LDS read per lane.  Every wave
+  // copies its own fragments (the last tile has no K/V copies to issue, and split this
+  // way no wave holds its SIMD partner up at the barrier) from a uniform base (the
+  // q-tile's first row) and a per-lane byte offset (query block and k-step; the
+  // instruction's own offset field would move the LDS destination too).  A partial
+  // q-tile repeats its last query (never written out).  The offsets stay below 2^31 when
+  // q_row * BQ < 2^30; otherwise each lane takes a 64-bit address.
   auto issue_q = [&](int p) __attribute__((always_inline)) {
-    // this wave's fragments are one contiguous run of 4 * KS KB; the LDS address advances
-    // copy by copy (opaque, so the compiler keeps one register, not one per copy)
-    uint32_t la = lds_addr(smem + (p % kStages) * Geo::STAGE + cwave * (4 * KS * 1024));
+    // the wave's fragments are one run of 2 * KS KB; the LDS address advances copy by
+    // copy (opaque, so the compiler keeps one register, not one per copy)
+    uint32_t la = lds_addr(smem + (p % kStages) * Geo::STAGE + wave * (2 * KS * 1024));
     const int qb0 = q0 + Geo::BQ;
     const uint16_t* qb = q + int64_t(qstart + qb0) * q_row + int64_t(g) * G * D;
     const bool off32 = q_row * Geo::BQ < (int64_t(1) << 30);
@@ -290,26 +289,22 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
       asm volatile("" : "+s"(la));
     };
 #pragma unroll
-    for (int wi = 0; wi < 2; ++wi) {
-      const int w = 2 * cwave + wi;
+    for (int j = 0; j < 2; ++j) {
+      const int qr = min((wave / G) * WQ + 16 * j + col, lq - 1 - qb0);   // row in the q-tile
+      const int eo = (wave % G) * D + 8 * quad;                            // element in the row
+      if (off32) {
+        const uint32_t voff = uint32_t((qr * q_row + eo) * 2);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int qr = min((w / G) * WQ + 16 * j + col, lq - 1 - qb0);   // row in the q-tile
-        const int eo = (w % G) * D + 8 * quad;                            // element in the row
-        if (off32) {
-          const uint32_t voff = uint32_t((qr * q_row + eo) * 2);
+        for (int ks = 0; ks < KS; ++ks) {
+          load_lds16_s_at(qb, voff + 64 * ks, la);
+          next();
+        }
+      } else {
+        const uint16_t* lp = qb + int64_t(qr) * q_row + eo;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            load_lds16_s_at(qb, voff + 64 * ks, la);
-            next();
-          }
-        } else {
-          const uint16_t* lp = qb + int64_t(qr) * q_row + eo;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            load_lds16_at(lp + 32 * ks, la);
-            next();
-          }
+        for (int ks = 0; ks < KS; ++ks) {
+          load_lds16_at(lp + 32 * ks, la);
+          next();
         }
       }
     }
@@ -385,6 +380,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // pair, the first key of the first one's last tile, which lies before its first
   // query's diagonal), so m is finite from then on.  Block 0's weights are computed while
   // block 1's QK MFMAs run.
+  bool fresh = true;                                  // the next half is a q-tile's first
   auto softmax_pv = [&](f32x4_t (&s)[2][2], int k0h, const bf16x8_t (&vf)[DT]) __attribute__((always_inline)) {
     const bool masked = (k0h + 31 > diag + wq0) || (k0h + 32 > lk);
     const float cs = masked ? 1.0f : scale_log2e;
@@ -403,6 +399,29 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     }
     uint32_t w[2][2][2];
     float hs[2];
+    if (fresh) {
+      // first half of a q-tile: m = -inf and O = l = 0, so the max is taken at once
+      // (a first pass of weights against -inf and a rescale of zeros would be thrown away)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float x = s[0][j][0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r) x = fmaxf(x, s[0][j][r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x = fmaxf(x, s[1][j][r]);
+        m[j] = xor32_max(xor16_max(x)) * cs;
+        hs[j] = weights(s[0][j], cs, m[j], w[0][j][0], w[0][j][1]) +
+                weights(s[1][j], cs, m[j], w[1][j][0], w[1][j][1]);
+        lsum[j] = hs[j];
+        const u32x4_t pw = {w[0][j][0], w[0][j][1], w[1][j][0], w[1][j][1]};
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+      fresh = false;
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) hs[j] = weights(s[0][j], cs, m[j], w[0][j][0], w[0][j][1]);
 #pragma unroll
@@ -522,7 +541,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // q) go out first and fly during this tile's math; ids go two positions further ahead.
   auto step = [&](int p, bool a_last, bool b_first) __attribute__((always_inline)) {
     if (a_last) {
-      if (has_b && copier) issue_q(p + 1);
+      if (has_b) issue_q(p + 1);
     } else if (p + 1 < nsteps) {
       issue_rows(p + 1, kbase, k_stride, 0);
       issue_rows(p + 1, vbase, v_stride, Geo::K_BYTES);
@@ -552,13 +571,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
         for (int ks = 0; ks < KS; ++ks)
           qf[j][ks] = *reinterpret_cast<const bf16x8_t*>(qw + (j * KS + ks) * 1024 + lane * 16);
       epilogue(qw);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        m[j] = -INFINITY;
-        lsum[j] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[j][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+      fresh = true;                                 // b's first half sets m, l and O
       q0 += Geo::BQ;
       wq0 += Geo::BQ;
       wkend = wq0 < lq ? diag + min(wq0 + WQ, lq) : 0;
