@@ -926,8 +926,8 @@ def prefill_counter_pass(dev):
                       "flop": legs}), flush=True)
 
 
-# Prefill legs told apart by grid (threads): (sequence x KV head) x q-tiles x 512.
-PREFILL_GRIDS = {"C3": 64 * 32 * 512, "C4": 128 * 8 * 512}
+# Prefill legs told apart by grid (threads): (sequence x KV head) x pairs of q-tiles x 512.
+PREFILL_GRIDS = {"C3": 64 * 16 * 512, "C4": 128 * 4 * 512}
 PREFILL_FLOP = {"C3": 275012124672, "C4": 171865800704}
 # bytes the leg must read at least once: q, the K/V rows its sequences span (C4: the
 # shared prefix once, every chunk), the tables
