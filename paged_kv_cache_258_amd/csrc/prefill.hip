@@ -33,6 +33,7 @@
 // fp32 path: a plain VALU kernel (one lane per query and head, online softmax), used
 //   for correctness-sized fp32 inputs.
 #include <math.h>
+#include <stdlib.h>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -112,17 +113,29 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
                     int64_t k_stride, int64_t v_stride,
                     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                     const int32_t* __restrict__ block_table, int32_t max_blocks,
-                    int32_t num_kv_heads, int32_t log2_bs, float scale_log2e,
+                    int32_t num_kv_heads, int32_t log2_bs, float scale_log2e, int32_t xcd_group,
                     uint16_t* __restrict__ out) {
   using Geo = PfGeom<D, G, NW>;
   constexpr int KS = Geo::KS, DT = Geo::DT, CPR = Geo::CPR, WQ = Geo::WQ;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Geo::SMEM];
   __shared__ int32_t s_ids[3][kMaxIds];               // block ids of positions p, p+1, p+2
 
-  const int pair = blockIdx.x;
-  const int b = pair / num_kv_heads;
-  const int g = pair - b * num_kv_heads;
-  const int qt = (gridDim.y - 1 - blockIdx.y) * (kPairQTiles ? 2 : 1);   // longest tiles first
+  // Workgroup L (launch order) runs on XCD L mod 8.  With xcd_group > 0 the (sequence x
+  // KV head) slices of each XCD are taken xcd_group at a time, longest pairs first within
+  // each group, so that fewer slices' K/V share the XCD's L2 at once; otherwise every
+  // slice's longest pairs come first.  (The host sets it only when the grid's x extent is
+  // a multiple of 8 * xcd_group.)
+  int slice = blockIdx.x, level = blockIdx.y;
+  if (xcd_group > 0) {
+    const int L = blockIdx.y * gridDim.x + blockIdx.x;
+    const int per_group = gridDim.y * xcd_group;
+    const int m = L >> 3, grp = m / per_group, r = m - grp * per_group;
+    level = r / xcd_group;
+    slice = (L & 7) + 8 * (grp * xcd_group + (r - level * xcd_group));
+  }
+  const int b = slice / num_kv_heads;
+  const int g = slice - b * num_kv_heads;
+  const int qt = (gridDim.y - 1 - level) * (kPairQTiles ? 2 : 1);   // longest tiles first
   const int qstart = cu_q[b];
   const int lq = cu_q[b + 1] - qstart;
   const int lk = cu_k[b + 1] - cu_k[b];
@@ -653,11 +666,24 @@ static hipError_t launch_bf16(const PrefillArgs& a, hipStream_t st) {
   const PagedArgs& p = a.p;
   const int qtiles = (a.max_seqlen_q + Geo::BQ - 1) / Geo::BQ;
   const int groups = kPairQTiles ? (qtiles + 1) / 2 : qtiles;   // workgroups per (sequence, KV head)
+  // XCD grouping: each XCD takes its slices in two halves, when a half still gives every CU
+  // of the XCD a workgroup (C3: 4 of 8 slices x 16 levels; C4: 8 of 16 x 4 levels).  One
+  // slice at a time per group, or a quarter, was slower (the XCD's CUs then wait on the
+  // last long pairs of a group); halves against one order over all slices: C3 265.9-266.9
+  // vs 271.5-273.3 us and 264.7-267.8 vs 267.9-271.4 us, C4 161.6-163.0 vs 163.1-164.4 us
+  // and 162.3-164.4 vs 163.1-165.1 us (two boxes).  NKV_PREFILL_XCD_GROUP
+  // in the environment (read at every call) sets the group size, 0 for one order.
+  const int slices = p.num_seqs * p.num_kv_heads;
+  const int cus_per_xcd = (p.num_cus > 0 ? p.num_cus : 256) / 8;
+  int xcd_group = slices % 16 == 0 ? slices / 16 : 0;
+  if (xcd_group * groups < cus_per_xcd) xcd_group = 0;
+  if (const char* e = getenv("NKV_PREFILL_XCD_GROUP")) xcd_group = atoi(e);
+  if (xcd_group <= 0 || slices % (8 * xcd_group) != 0 || 8 * xcd_group >= slices) xcd_group = 0;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW>), dim3(p.num_seqs * p.num_kv_heads, groups),
                      dim3(Geo::NT), 0, st, static_cast<const uint16_t*>(a.q), a.q_row_elems,
                      static_cast<const uint16_t*>(p.k_cache), static_cast<const uint16_t*>(p.v_cache),
                      a.k_row_elems, a.v_row_elems, a.cu_seqlens_q, a.cu_seqlens_k, p.block_table, p.max_blocks_per_seq,
-                     p.num_kv_heads, p.log2_block_size, p.scale_log2e,
+                     p.num_kv_heads, p.log2_block_size, p.scale_log2e, xcd_group,
                      static_cast<uint16_t*>(a.out));
   return hipGetLastError();
 }
