@@ -65,6 +65,11 @@
  * positions in [0, max_position) -- waits for the stream, and returns NKV_ERR_INVALID_ARG (naming the violation and
  * the first offending token or sequence) without launching the operation.  It
  * allocates nothing but synchronises the stream: a debugging aid, not for hot loops.
+ *
+ * Tuning: NKV_PREFILL_XCD_GROUP=n in the environment (read at every bf16 prefill call)
+ * sets how many (sequence, KV head) slices each XCD takes at a time (0: one longest-first
+ * order over all of them); the default is half of an XCD's slices when that still gives
+ * each of its CUs a workgroup.  It changes the order of work only, never the results.
  */
 #ifndef NKV_H
 #define NKV_H
