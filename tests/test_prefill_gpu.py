@@ -171,6 +171,20 @@ def test_prefill_deterministic_and_block_permutation_invariant():
     assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
 
 
+@pytest.mark.parametrize("group", ["0", "1", "2", "4"])
+def test_prefill_work_order_bitwise(group, monkeypatch):
+    """The order in which each XCD takes its (sequence, KV head) slices (NKV_PREFILL_XCD_GROUP,
+    read at every call; C4's default takes them in halves of 8) changes which workgroup runs
+    when, never what one computes: every order gives the default's bits."""
+    dev = require_gpu()
+    prefix, case = wl.c4_prefix_chunk(dev)
+    monkeypatch.delenv("NKV_PREFILL_XCD_GROUP", raising=False)
+    ref_out = gpu_prefill(case, prefix)
+    monkeypatch.setenv("NKV_PREFILL_XCD_GROUP", group)
+    out = gpu_prefill(case, prefix)
+    assert torch.equal(ref_out.view(torch.int16), out.view(torch.int16))
+
+
 @pytest.mark.parametrize("direction", [1.0, -1.0])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_logits_ramp_forces_rescales(direction, dtype):
