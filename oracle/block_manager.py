@@ -17,7 +17,7 @@ What the pages fix:
   sequences with the same prefix point at the same physical block and its K/V is stored
   once.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * hash of a full block: 64-bit FNV-1a (Fowler/Noll/Vo, the published offset basis and
   prime) over the previous block's hash (8 bytes, little-endian; absent for a sequence's

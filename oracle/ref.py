@@ -31,7 +31,7 @@ What is computed, and where the pages define it:
   cached): sequence ``b``'s keys are rows ``cu_seqlens_k[b]..cu_seqlens_k[b+1]`` of
   the flat ``[Tk, Hkv, D]`` k and v (「同一个 Qwen3，两种写法」 §3.2).
 
-Readings where the pages are silent (each listed with its reason in the design doc):
+Readings where the pages are silent, each with its reason:
   * causal alignment when a chunk has fewer queries than keys: bottom-right --
     query ``i`` of a segment with ``Lq`` queries and ``Lk`` keys sits at absolute
     position ``Lk - Lq + i`` and sees keys ``j <= Lk - Lq + i``;

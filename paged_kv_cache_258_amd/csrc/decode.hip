@@ -154,8 +154,8 @@ __device__ __forceinline__ void store_elem(typename S::elem* p, float x) {
 // are written as partials (max, sum, weighted values) and merged by
 // decode_fixup_kernel.  The assignment depends only on the lengths, so results are
 // reproducible and independent of the physical block layout.  The K/V copies carry the
-// nontemporal hint: a step reads each cached row once, and with the hint the C2-sized
-// step (64 sequences, 8 KV heads, 595 MB) went from 115 to 105 us.
+// nontemporal hint: a step reads each cached row once, and with the hint a step of 64
+// sequences with 512-4096 cached tokens (8 KV heads, 595 MB) went from 115 to 105 us.
 
 #ifndef NKV_SK_STAGES
 #define NKV_SK_STAGES 4
@@ -578,10 +578,10 @@ __global__ void __launch_bounds__(64)
 decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_t num_kv_heads,
                     int32_t W, const float* __restrict__ ws_part, const float* __restrict__ ws_ml,
                     int32_t* __restrict__ ws_claim, uint16_t* __restrict__ out) {
-  constexpr int C4 = D / 4;                  // 16-byte chunks of a partial row
-  constexpr int PG = 64 / C4;                // pieces per pass
+  constexpr int NCH = D / 4;                  // 16-byte chunks of a partial row
+  constexpr int PG = 64 / NCH;                // pieces per pass
   constexpr int NP = kFixPieces / PG;        // passes per chunk
-  static_assert(C4 <= 64 && 64 % C4 == 0 && kFixPieces % PG == 0, "unsupported head_dim");
+  static_assert(NCH <= 64 && 64 % NCH == 0 && kFixPieces % PG == 0, "unsupported head_dim");
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int g = h / G;
@@ -601,7 +601,7 @@ decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_
     const int k = sp.start(w) >= s ? 0 : 1;
     return (w * 2 + k) * G + col;
   };
-  const int c = lane % C4, pg = lane / C4;
+  const int c = lane % NCH, pg = lane / NCH;
   float M = -INFINITY, den = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   // Issue every load of the chunk at c0.  Lane i < kFixPieces locates piece c0 + i once
@@ -650,14 +650,14 @@ decode_fixup_kernel(const int32_t* __restrict__ prefix, int32_t num_seqs, int32_
     if (c0 + 2 * kFixPieces < np) load(c0 + 2 * kFixPieces, ra, ma, la);
     consume(rb, mb, lb);
   }
-  // sum the PG piece groups (lanes c, c + C4, ...) in a fixed order
+  // sum the PG piece groups (lanes c, c + NCH, ...) in a fixed order
 #pragma unroll
-  for (int off = C4; off < 64; off <<= 1) {
+  for (int off = NCH; off < 64; off <<= 1) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], off);
     den += __shfl_xor(den, off);
   }
-  if (lane < C4) {
+  if (lane < NCH) {
     const float inv = 1.0f / den;
     const int64_t orow = int64_t(b) * num_kv_heads * G + h;
     const u32x2_t w2 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};

@@ -204,7 +204,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // instruction until the CU takes it, slowly for a whole tile's worth: issued by all
   // waves at the top of a tile they held both waves of every SIMD (about 1500 cycles per
   // tile); issued by one wave of each SIMD pair (w, w + NW/2), the partner computes
-  // meanwhile (C3 loop 3.80 -> 3.49 us per tile).
+  // meanwhile (8 prompts of 2048 tokens: the loop from 3.80 to 3.49 us per tile).
   const bool copier = wave < Geo::CW;
   const int cwave = wave % Geo::CW;
   // Copy j of a copying wave fills LDS slots (cwave * K_DMA + j) * 64 + lane: the lane's
@@ -231,7 +231,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   // the rows are at most kBK - 1 strides from its base; with strides below 2^23 elements
   // the byte offsets fit 32 bits, so a copy of a full tile is a wave-uniform base (the
   // tile's, plus j * RPI rows) and a per-lane offset fixed for the whole kernel (one of
-  // NE) instead of 64-bit lane arithmetic (C3 310 -> 304 us).
+  // NE) instead of 64-bit lane arithmetic (8 prompts of 2048 tokens: 310 -> 304 us).
   const bool off32 = k_stride < (int64_t(1) << 23) && v_stride < (int64_t(1) << 23);
   uint32_t koff[NE], voff[NE];
 #pragma unroll
@@ -516,7 +516,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
         if (qi < lq) {
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ost + row * (D * 2) + (cc ^ (row & (CPR - 1))) * 16);
           // nontemporal: the output is not read again here, and cached it would evict K/V lines
-          // that the other workgroups of the sequence still read from L2 (C3 275 -> 262 us)
+          // that the other workgroups of the sequence still read from L2 (8 prompts of 2048
+          // tokens: 275 -> 262 us)
           __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (int64_t(qstart + qi) * hq + h) * D + cc * 8));
         }
       }
@@ -667,12 +668,14 @@ static hipError_t launch_bf16(const PrefillArgs& a, hipStream_t st) {
   const int qtiles = (a.max_seqlen_q + Geo::BQ - 1) / Geo::BQ;
   const int groups = kPairQTiles ? (qtiles + 1) / 2 : qtiles;   // workgroups per (sequence, KV head)
   // XCD grouping: each XCD takes its slices in two halves, when a half still gives every CU
-  // of the XCD a workgroup (C3: 4 of 8 slices x 16 levels; C4: 8 of 16 x 4 levels).  One
-  // slice at a time per group, or a quarter, was slower (the XCD's CUs then wait on the
-  // last long pairs of a group); halves against one order over all slices: C3 265.9-266.9
-  // vs 271.5-273.3 us and 264.7-267.8 vs 267.9-271.4 us, C4 161.6-163.0 vs 163.1-164.4 us
-  // and 162.3-164.4 vs 163.1-165.1 us (two boxes).  NKV_PREFILL_XCD_GROUP
-  // in the environment (read at every call) sets the group size, 0 for one order.
+  // of the XCD a workgroup (8 prompts of 2048 tokens, 8 KV heads: 4 of an XCD's 8 slices
+  // x 16 levels; 16 chunks of 512 tokens after a 1024-token prefix: 8 of 16 x 4 levels).
+  // One slice at a time per group, or a quarter, was slower (the XCD's CUs then wait on
+  // the last long pairs of a group); halves against one order over all slices, on two
+  // boxes: 265.9-266.9 vs 271.5-273.3 us and 264.7-267.8 vs 267.9-271.4 us for the 2048-
+  // token prompts, 161.6-163.0 vs 163.1-164.4 us and 162.3-164.4 vs 163.1-165.1 us for the
+  // chunks.  NKV_PREFILL_XCD_GROUP in the environment (read at every call) sets the group
+  // size, 0 for one order.
   const int slices = p.num_seqs * p.num_kv_heads;
   const int cus_per_xcd = (p.num_cus > 0 ? p.num_cus : 256) / 8;
   int xcd_group = slices % 16 == 0 ? slices / 16 : 0;

@@ -422,7 +422,7 @@ def test_prefill_pair_count_matches_mask():
     cu_q = np.concatenate([[0], np.cumsum(seqs_q)])
     cu_k = np.concatenate([[0], np.cumsum(seqs_k)])
     assert acc.prefill_pairs(cu_q, cu_k) == int(brute.varlen_causal_mask(seqs_q, seqs_k).sum())
-    # the survey's C3 / C4 totals
+    # 8 prompts of 2048 tokens; 16 chunks of 512 queries after a 1024-token prefix (32 q heads, D 128)
     c3 = np.arange(0, 16385, 2048)
     assert acc.prefill_flops(c3, c3, 32, 128) == 275_012_124_672
     c4q = np.arange(0, 8193, 512)
