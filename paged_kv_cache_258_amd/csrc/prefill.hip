@@ -20,14 +20,15 @@
 //   in the key order of the P^T operand.  The next tile's copies are in flight while the current
 //   tile is computed.
 //   Scores are computed transposed, S^T = K Q^T, in 16x16 blocks: a lane holds 4 keys of
-//   one query per block, so the max of a query spans four lanes and its row sum stays in
-//   the lanes until the end.  P goes from the S^T accumulators straight into the B
+//   one query per block, so the max of a query spans four lanes.  P goes from the S^T accumulators straight into the B
 //   operand of O^T += V^T P^T.  A tile is processed as four 32-key halves, each QK ->
 //   softmax -> PV; the 16x16 blocks let the softmax of the half's first key block start
 //   after 4 of the QK MFMAs instead of all of them (a 32x32 block needs every k-step).
 //   The softmax uses one FMA + exp2 per score (scale folded in), the running max is
 //   raised lazily (rescale only past 2^8 headroom, detected from the weights' sum), and
-//   the row sum is a dot2 of the rounded bf16 weights.  Only halves that cross the
+//   the row sum of the rounded bf16 weights comes from one more MFMA per query block and
+//   half, with a fragment of ones in place of V^T, which hands every lane of a query its
+//   full sum (8 dot2 per half on the VALU cost more than the 2 MFMAs).  Only halves that cross the
 //   causal diagonal or the end of the keys are masked.  The output goes through LDS so
 //   each row is written as one contiguous run, with nontemporal stores.
 // fp32 path: a plain VALU kernel (one lane per query and head, online softmax), used
@@ -376,15 +377,20 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
   auto weights = [&](const f32x4_t& s, float cs, float mq, uint32_t& w0, uint32_t& w1) __attribute__((always_inline)) {
     w0 = pack_bf16x2(fast_exp2(fmaf(s[0], cs, -mq)), fast_exp2(fmaf(s[1], cs, -mq)));
     w1 = pack_bf16x2(fast_exp2(fmaf(s[2], cs, -mq)), fast_exp2(fmaf(s[3], cs, -mq)));
-    return dot2_bf16(w1, ones, dot2_bf16(w0, ones, 0.f));
+  };
+  const bf16x8_t onesf = __builtin_bit_cast(bf16x8_t, u32x4_t{ones, ones, ones, ones});
+  // Row sums of one query block's weights in a half: ones^T P^T puts the sum over the 32
+  // keys of query col in every output element of that column, so each lane reads its own.
+  auto rowsum = [&](const bf16x8_t& pf) __attribute__((always_inline)) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(onesf, pf, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0)[0];
   };
   // Softmax and P.V of one half.  s[i][j] is S^T of key block i and query block j; a
   // lane holds keys 16i + 4*quad + r of query 16j + col.  Masked halves are scaled
   // before the mask is applied (cs = 1 afterwards) so that a zero softmax_scale cannot
   // turn -inf into NaN; unmasked halves fold the scale into the exponent's FMA.  The
   // running max m is raised lazily and without a max pass in the common case: the
-  // weights are taken against the current m, and only when some lane's sum of its 8
-  // rounded weights of a query block exceeds kLazyBound (or is not finite: m = -inf
+  // weights are taken against the current m, and only when some query's sum of its 32
+  // rounded weights in the half exceeds kLazyBound (or is not finite: m = -inf
   // before the first half) does the wave raise m to the max of the half's scores of
   // that block (over the four lanes of each query), rescale O and l, and take the
   // weights again.  Every weight is at most that sum, so no weight kept exceeds
@@ -412,6 +418,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     }
     uint32_t w[2][2][2];
     float hs[2];
+    bf16x8_t pf[2];
     if (fresh) {
       // first half of a q-tile: m = -inf and O = l = 0, so the max is taken at once
       // (a first pass of weights against -inf and a rescale of zeros would be thrown away)
@@ -423,22 +430,25 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
 #pragma unroll
         for (int r = 0; r < 4; ++r) x = fmaxf(x, s[1][j][r]);
         m[j] = xor32_max(xor16_max(x)) * cs;
-        hs[j] = weights(s[0][j], cs, m[j], w[0][j][0], w[0][j][1]) +
-                weights(s[1][j], cs, m[j], w[1][j][0], w[1][j][1]);
-        lsum[j] = hs[j];
-        const u32x4_t pw = {w[0][j][0], w[0][j][1], w[1][j][0], w[1][j][1]};
-        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+        weights(s[0][j], cs, m[j], w[0][j][0], w[0][j][1]);
+        weights(s[1][j], cs, m[j], w[1][j][0], w[1][j][1]);
+        pf[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0][j][0], w[0][j][1], w[1][j][0], w[1][j][1]});
+        lsum[j] = rowsum(pf[j]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[j], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       }
       fresh = false;
       return;
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) hs[j] = weights(s[0][j], cs, m[j], w[0][j][0], w[0][j][1]);
+    for (int j = 0; j < 2; ++j) weights(s[0][j], cs, m[j], w[0][j][0], w[0][j][1]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) hs[j] += weights(s[1][j], cs, m[j], w[1][j][0], w[1][j][1]);
+    for (int j = 0; j < 2; ++j) {
+      weights(s[1][j], cs, m[j], w[1][j][0], w[1][j][1]);
+      pf[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0][j][0], w[0][j][1], w[1][j][0], w[1][j][1]});
+      hs[j] = rowsum(pf[j]);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (__any(!(hs[j] <= kLazyBound))) {
@@ -453,15 +463,15 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[j][dt] *= alpha;
         m[j] = mn;
-        hs[j] = weights(s[0][j], cs, mn, w[0][j][0], w[0][j][1]) +
-                weights(s[1][j], cs, mn, w[1][j][0], w[1][j][1]);
+        weights(s[0][j], cs, mn, w[0][j][0], w[0][j][1]);
+        weights(s[1][j], cs, mn, w[1][j][0], w[1][j][1]);
+        pf[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0][j][0], w[0][j][1], w[1][j][0], w[1][j][1]});
+        hs[j] = rowsum(pf[j]);
       }
       lsum[j] += hs[j];
-      const u32x4_t pw = {w[0][j][0], w[0][j][1], w[1][j][0], w[1][j][1]};
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[j][dt], 0, 0, 0);
+        o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[j], o[j][dt], 0, 0, 0);
     }
   };
   // One 32-key half: QK of key block 0 for both query blocks, then of key block 1 (the
@@ -493,8 +503,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_row,
     const int col = ln & 15, quad = ln >> 4;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      // the four lanes of a query hold different keys
-      const float inv = 1.0f / xor32_sum(xor16_sum(lsum[j]));
+      // every lane of a query holds its whole row sum (from the ones MFMA)
+      const float inv = 1.0f / lsum[j];
       if (wq0 + 16 * j < lq) {
         const int r = 16 * j + col;
 #pragma unroll
