@@ -92,7 +92,10 @@ qk_norm_rope_store_kernel(const uint16_t* __restrict__ qkv, int64_t qkv_row,
     const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(row + H2 + fi);
     const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(row + H2 + fi + 4);
     const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-    const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    // the sine with the sign of this lane's half: o = y c + y' sn (negation is exact)
+    float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sn[i] = second ? sn[i] : -sn[i];
     const uint16_t* src = qkv + int64_t(t) * qkv_row;
     for (int sb = 0; sb < nslots; sb += GL * KR) {
       u32x4_t a[KR];
@@ -139,7 +142,7 @@ qk_norm_rope_store_kernel(const uint16_t* __restrict__ qkv, int64_t qkv_row,
         unpack8(pw, yp);
 #pragma unroll
         for (int i = 0; i < 8; ++i)   // first half: y1 c - y2 s; second half: y2 c + y1 s
-          o[i] = second ? y[i] * c[i] + yp[i] * sn[i] : y[i] * c[i] - yp[i] * sn[i];
+          o[i] = y[i] * c[i] + yp[i] * sn[i];
         const u32x4_t ow = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
                             pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
         uint16_t* dst = nullptr;
