@@ -9,8 +9,9 @@
 // with the cast back to the input dtype before the weight product).
 //
 // Without fusion, q and k make three round trips through HBM (norm, rope, store); here
-// the projection output is read once and each result written once, both with the
-// nontemporal hint (for 16384 tokens of Qwen3-8B heads: 84 -> 75 us).
+// the projection output is read once with plain loads and each result written once with
+// the nontemporal hint (16384 tokens of Qwen3-8B heads: 69 us; 77 us with nontemporal
+// loads too, 84 us with neither hint).
 //
 // Layout of the work: one wave per token (grid-stride over tokens), so the position, the
 // slot, the cos/sin row and the norm weights are read once per token and every head's
@@ -102,7 +103,7 @@ qk_norm_rope_store_kernel(const uint16_t* __restrict__ qkv, int64_t qkv_row,
 #pragma unroll
       for (int k = 0; k < KR; ++k) {                      // every load of the pass first
         const int s = sb + k * GL + g;
-        a[k] = s < nslots ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + int64_t(s) * D + 8 * j))
+        a[k] = s < nslots ? *reinterpret_cast<const u32x4_t*>(src + int64_t(s) * D + 8 * j)
                           : u32x4_t{0, 0, 0, 0};
       }
 #pragma unroll
