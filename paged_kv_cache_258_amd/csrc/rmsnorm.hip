@@ -16,8 +16,8 @@
 // added in a fixed order so every thread gets the same bits), and writes only its own
 // chunks after it has read them.  So the output may alias the hidden state and the new
 // residual may alias the residual (the in-place use).  Rows are touched once, so their
-// loads and stores are nontemporal (the weight, read by every row, is not): in a sweep
-// of 16384 x 4096 rows that took the kernel from 98 to 80 us, about 6.7 TB/s.  The grid
+// stores are nontemporal; their loads are plain (16384 x 4096 rows: 77 us, about 7 TB/s,
+// against 91 us with nontemporal loads, and 98 us with neither hint).  The grid
 // has a workgroup per row up to 64 per CU.  Float contraction is off so that
 // products and sums round as float32 tensor arithmetic does; the mean is a correctly
 // rounded division and the reciprocal root is v_rsq_f32 (within an ulp).
@@ -66,9 +66,9 @@ add_rms_norm_kernel(const uint16_t* x, const uint16_t* residual,
     for (int k = 0; k < CPT; ++k) {   // every load of the row first
       const int c = tid + k * kNormThreads;
       if (c < chunks) {
-        xa[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + row + 8 * c));
+        xa[k] = *reinterpret_cast<const u32x4_t*>(x + row + 8 * c);
         if (residual)
-          ra[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(residual + row + 8 * c));
+          ra[k] = *reinterpret_cast<const u32x4_t*>(residual + row + 8 * c);
       }
     }
     float v[CPT][8];
