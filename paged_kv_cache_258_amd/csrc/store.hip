@@ -9,6 +9,8 @@
 // loads issued before the stores).  The slot is loaded once per wave.  Waves walk the
 // tokens grid-stride so the launch fills every CU without one workgroup per token.
 // The copy is a bit copy: no type conversion, so bf16 and fp32 share the kernel.
+// The pool rows are written with the nontemporal hint (16384 tokens of 8 KV heads x 128:
+// 23.8 vs 25.4 us per call; 512 tokens x 16 chunks back to back: 10.0 vs 11.0 us).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,8 +50,8 @@ store_kvcache_kernel(const char* __restrict__ key, int64_t key_row_bytes,
       for (int u = 0; u < kStoreUnroll; ++u) {
         const int i = base + u * kWave + lane;
         if (i < row_vecs) {
-          kdst[i] = kb[u];
-          vdst[i] = vb[u];
+          __builtin_nontemporal_store(kb[u], kdst + i);
+          __builtin_nontemporal_store(vb[u], vdst + i);
         }
       }
     }
